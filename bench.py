@@ -1,0 +1,188 @@
+"""Throughput of batched Newton-Schulz orthogonalization on one MI355X.
+
+Default workload: 8 bf16 matrices of 8192x6144, each rank-64 plus 1e-3 noise
+(seeded), 5 quintic steps per matrix. One "step" of this benchmark is one
+ns_orthogonalize_batched call over the whole 8-matrix batch: norm,
+normalize/transpose, 5 x (X X^T, bA + cA^2, aX + BX), write-back.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line. `value` is matrices per second with the inputs already
+resident in HBM; FLOPs per matrix follow 5 * (4 m^2 n + 2 m^3), m = min dim.
+Every timed step works on its own resident copy of the batch (restored from a
+pristine copy before the timed region), so no step reuses an output.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NS-orthogonalized matrices/s + TFLOP/s (% bf16 MFMA peak), 8192x6144 bf16"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_workload(name):
+    import torch
+    from newton_schulz_04_amd import workloads as wl
+    if name == "dense_lowrank":
+        mats = [wl.dense_lowrank_matrix(i) for i in range(wl.DENSE_COUNT)]
+        desc = {"workload": "dense_lowrank", "matrices": 8, "shape": [8192, 6144],
+                "dtype": "bf16", "input": "rank-64 L@R + 1e-3*N(0,1), seed 2", "ns_steps": 5}
+    elif name.startswith("ragged_remainder_"):
+        r = int(name.rsplit("_", 1)[1])
+        mats = [c.mat for c in wl.ragged_remainder(r, world=64, padded=True)]
+        desc = {"workload": name, "matrices": r, "shape": [8192, 6144], "dtype": "bf16",
+                "input": "N(0,1), seed 3", "ns_steps": 5}
+    elif name == "moe_mixed":
+        g = torch.Generator(device="cuda").manual_seed(4)
+        mats = [torch.randn(s, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                for s in wl.moe_mixed_shapes()]
+        desc = {"workload": "moe_mixed", "matrices": len(mats), "dtype": "bf16",
+                "input": "N(0,1) drawn on the GPU (timing only)", "ns_steps": 5}
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return mats, desc
+
+
+def cpu_baseline(sample_rows=4096, sample_cols=3072):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload: one
+    Newton-Schulz step on the top-left sample_rows x sample_cols block of
+    matrix 0. Scaled to matrices/s by metric FLOPs (an optimistic scaling for
+    the CPU: the oracle gets slower, not faster, at the full size)."""
+    import numpy as np
+    from newton_schulz_04_amd import workloads as wl
+    from oracle import oracle
+    g = wl.dense_lowrank_matrix(0)[:sample_rows, :sample_cols].float().numpy()
+    m, n = min(g.shape), max(g.shape)
+    flops = 4 * m * m * n + 2 * m ** 3
+    t0 = time.time()
+    oracle.newton_schulz(g, steps=1, coeffs=oracle.QUINTIC)
+    dt = time.time() - t0
+    per_matrix = wl.flops_per_matrix(*wl.DENSE_SHAPE)
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": round(flops / dt / per_matrix, 6), "unit": "matrices/s", "cores": cores,
+            "kind": "oracle", "gflops_fp64": round(flops / dt / 1e9, 3), "seconds": round(dt, 2),
+            "sample": f"1 NS step of the top-left {sample_rows}x{sample_cols} block of matrix 0 "
+                      f"(fp64, plain loops + OpenMP), scaled by metric FLOPs to 8192x6144 x 5 steps"}
+
+
+def metric_flops_per_kind(shapes):
+    """Metric FLOPs of one launch of each GEMM stage over the batch (each
+    product counted in full: X X^T 2m^2n, A A 2m^3, B X 2m^2n)."""
+    f = {"syrk": 0, "poly": 0, "update": 0}
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        if m <= 32 or m == 0:
+            continue
+        f["syrk"] += 2 * m * m * n
+        f["poly"] += 2 * m ** 3
+        f["update"] += 2 * m * m * n
+    return f
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense_lowrank")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("only --gpus 1 is supported: the batched Newton-Schulz path runs on one GPU")
+        sys.exit(2)
+
+    import torch
+    import newton_schulz_04_amd as ns
+    from newton_schulz_04_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    log(f"library {ns.version()}; generating workload {args.workload}")
+    mats, desc = make_workload(args.workload)
+    shapes = [tuple(m.shape) for m in mats]
+    flops_batch = sum(wl.flops_per_matrix(r, c) for r, c in shapes)
+    pristine = [m.cuda() for m in mats]
+    del mats
+    nbatch = max(1, min(args.steps, 16))
+    batches = [[p.clone() for p in pristine] for _ in range(nbatch)]
+    torch.cuda.synchronize()
+    log(f"{len(shapes)} matrices, {flops_batch / 1e12:.3f} TFLOP per step, {nbatch} resident copies")
+
+    for w in range(args.warmup):
+        ns.orthogonalize(batches[w % nbatch])
+        torch.cuda.synchronize()
+        log(f"warmup {w + 1}/{args.warmup} done")
+    for b in batches:
+        for dst, src in zip(b, pristine):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+
+    ns.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ns.orthogonalize(batches[k % nbatch])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ns.profile_enable(False)
+    prof = ns.profile_read()
+    elapsed = t1 - t0
+    log(f"timed {args.steps} steps in {elapsed:.3f} s")
+
+    per_kind = metric_flops_per_kind(shapes)
+    kernels = {}
+    for kind, (ms, n) in prof.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        entry = {"ms_avg": round(avg, 4), "launches": n, "ms_total": round(ms, 3)}
+        if kind in per_kind and per_kind[kind]:
+            entry["tflops"] = round(per_kind[kind] / (avg * 1e-3) / 1e12, 1)
+        kernels[kind] = entry
+    dom = max((k for k in kernels if k in per_kind), key=lambda k: kernels[k]["ms_total"])
+    achieved = per_kind[dom] / (kernels[dom]["ms_avg"] * 1e-3) / 1e12
+    ms_per_step = elapsed / args.steps * 1e3
+    tflops = flops_batch / (elapsed / args.steps) / 1e12
+    value = len(shapes) * args.steps / elapsed
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": desc,
+        "tflops": round(tflops, 1),
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            log("timing the CPU oracle on a bounded sample")
+            out["cpu_baseline"] = cpu_baseline()
+        except Exception as e:  # the oracle is optional for the GPU figure
+            out["cpu_baseline"] = {"error": str(e)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

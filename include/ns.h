@@ -1,0 +1,169 @@
+/*
+ * ns.h -- C ABI of libns.so: batched Newton-Schulz orthogonalization on
+ * MI355X (gfx950).
+ *
+ * The operation. Each matrix G (rows x cols, row-major) of a batch is replaced
+ * in place by its Newton-Schulz orthogonalization, Muon's quintic iteration
+ * (K. Jordan et al., "Muon: An optimizer for hidden layers in neural
+ * networks", 2024):
+ *
+ *     X = G / (||G||_F + 1e-7)
+ *     if rows > cols: X = X^T                    (X is m x n, m <= n)
+ *     repeat `steps` times:  A = X X^T;  B = b A + c A^2;  X = a X + B X
+ *     if transposed: X = X^T;  G <- X rounded to the buffer's dtype
+ *
+ * The pages this library is built from name this operation as the compute
+ * that Muon-family optimizers run on every assembled 2-D update matrix
+ * (microsoft/dion PR #74, "Fix megabatch_orthogonalize_async hang on empty
+ * FSDP2 shards", Fix section, which also states that zero rows stay zero) and
+ * rank its cost as max(M,N)*min(M,N)^2 (NVIDIA/Megatron-LM PR #6379, "Balance
+ * LayerWise optimizer shards by Newton-Schulz cost, not parameter size",
+ * Changes item 1). They do not give the coefficients; (a, b, c) =
+ * (3.4445, -4.7750, 2.0315) with 5 steps is the usual choice and what
+ * NS_QUINTIC_* below hold.
+ *
+ * Precision. bf16 matrices: products on bf16 MFMA with fp32 accumulation, an
+ * fp32 master copy of X carried between steps, result rounded to bf16
+ * (round-to-nearest-even); matrices with min(rows, cols) <= 32 run the whole
+ * iteration in fp32. fp32 matrices: fp32 arithmetic throughout.
+ * Zero rows and columns of G come back as exact +0.0.
+ *
+ * Threading. Entry points may be called from several host threads; calls
+ * that share a (device, stream) pair are serialized on a lock. All GPU work
+ * is enqueued on the caller's stream and no entry point waits for the device,
+ * except ns_profile_read and ns_release_workspace as documented.
+ */
+#ifndef NS_H
+#define NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NS_BF16 = 0, /* bfloat16 storage */
+    NS_FP32 = 1  /* float32 storage  */
+} ns_dtype;
+
+typedef enum {
+    NS_OK = 0,      /* success (work enqueued)                                */
+    NS_EINVAL = 1,  /* invalid argument; nothing was enqueued                 */
+    NS_EDTYPE = 2,  /* unknown dtype; nothing was enqueued                    */
+    NS_ENOMEM = 3,  /* device or host allocation failed; nothing enqueued     */
+    NS_EHIP = 4     /* a HIP call or kernel launch failed; see ns_last_error  */
+} ns_status;
+
+#define NS_QUINTIC_A 3.4445f
+#define NS_QUINTIC_B (-4.7750f)
+#define NS_QUINTIC_C 2.0315f
+
+/*
+ * Orthogonalize `count` matrices in place.
+ *
+ *   ptrs    host array of `count` device pointers. ptrs[i] points at matrix i:
+ *           shapes[2i] x shapes[2i+1] elements of `dtype`, row-major and
+ *           contiguous (leading dimension = cols), aligned to the element
+ *           size. Read as G, overwritten with the result. Matrices must not
+ *           overlap. A pointer may be NULL only for an empty matrix.
+ *   shapes  host array of 2*count int64: (rows, cols) per matrix, each >= 0.
+ *           rows == 0 or cols == 0 is an empty matrix (an empty shard): it is
+ *           accepted and never touched.
+ *   count   number of matrices, >= 0; 0 enqueues nothing.
+ *   steps   iterations, >= 0. steps == 0 writes G / (||G||_F + 1e-7).
+ *   coeffs  host array of 3 floats (a, b, c) applied at every step; may be
+ *           NULL only when steps == 0.
+ *   dtype   an ns_dtype; all matrices of a call share it.
+ *   stream  a hipStream_t (NULL = the legacy default stream) on the current
+ *           device. All work is enqueued on it; the results are complete in
+ *           stream order. Host arrays are only read before the call returns.
+ *
+ * Workspace: the library keeps a device workspace per (device, stream) pair,
+ * grown on demand with stream-ordered allocation, plus a small cache of batch
+ * plans keyed by the argument values. Two calls on the same stream are
+ * ordered by the stream; calls on different streams use separate workspaces.
+ *
+ * Errors: NS_EINVAL (negative count/steps/shape, NULL ptrs/shapes with
+ * count > 0, NULL pointer for a non-empty matrix, NULL coeffs with steps > 0,
+ * a dimension above 2^24), NS_EDTYPE, NS_ENOMEM, NS_EHIP. On any error the
+ * message is available from ns_last_error(). NaN and Inf propagate unchecked.
+ */
+ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes,
+                                   int32_t count, int32_t steps,
+                                   const float* coeffs, int32_t dtype,
+                                   void* stream);
+
+/*
+ * Device workspace bytes a call with these shapes and dtype needs (host-only;
+ * touches no device). Same validation of shapes/count/dtype as above.
+ */
+ns_status ns_workspace_bytes(const int64_t* shapes, int32_t count,
+                             int32_t dtype, size_t* out_bytes);
+
+/*
+ * Free the workspace and plan cache held for (current device, stream).
+ * Device memory is released with stream-ordered frees on `stream`, so this is
+ * safe while earlier calls are in flight; the pinned host staging buffers are
+ * freed after a host wait for their pending uploads. Returns NS_OK if nothing
+ * was held.
+ */
+ns_status ns_release_workspace(void* stream);
+
+/* Message of the last non-OK status on the calling thread ("" if none). */
+const char* ns_last_error(void);
+
+/* Library version string. */
+const char* ns_version(void);
+
+/*
+ * Newton-Schulz cost of a rows x cols matrix, max(M,N) * min(M,N)^2, the
+ * model the Megatron-LM page (PR #6379, Changes item 1) ranks work by and the
+ * batch scheduler orders matrices by. 0 for an empty matrix, -1 for a
+ * negative dimension. Host-only.
+ */
+int64_t ns_compute_cost(int64_t rows, int64_t cols);
+
+/*
+ * Host-only view of the batch plan, for tests and tools.
+ *
+ * ns_plan_classify: kinds[i] = 0 (empty), 1 (small: whole iteration in one
+ * workgroup, fp32), 2 (large: tiled MFMA path).
+ *
+ * ns_plan_tiles: the tile list of one grouped GEMM stage in launch order.
+ *   stage 0 = A = X X^T (upper-triangle tiles), 1 = B = bA + cA^2 (same
+ *   tiles), 2 = X <- aX + BX (all tiles). Each tile is 4 int32:
+ *   (matrix index into the caller's batch, block row, block column, K depth
+ *   in elements). Writes min(capacity, total) tiles to `out` (which may be
+ *   NULL when capacity is 0) and the total count to *n_tiles.
+ *   *tile_size receives the tile edge in elements.
+ */
+ns_status ns_plan_classify(const int64_t* shapes, int32_t count, int32_t dtype,
+                           int32_t* kinds);
+ns_status ns_plan_tiles(const int64_t* shapes, int32_t count, int32_t dtype,
+                        int32_t stage, int32_t* out, int64_t capacity,
+                        int64_t* n_tiles, int32_t* tile_size);
+
+/*
+ * Per-kernel timing with HIP events recorded on the call's stream around
+ * every launch the library makes while profiling is on.
+ *
+ * Kinds: 0 norm partial sums, 1 norm finalize, 2 normalize/transpose/pad,
+ * 3 X X^T, 4 bA + cA^2, 5 aX + BX (and final write-back), 6 small-matrix
+ * fused kernel, 7 steps==0 write-back.
+ *
+ * ns_profile_enable(1) clears the accumulators and starts recording;
+ * ns_profile_enable(0) stops. ns_profile_read waits for every recorded event
+ * (a host wait on the events only), then writes, for the first n_kinds kinds,
+ * the total milliseconds and the launch count since the last clear.
+ */
+#define NS_PROFILE_KINDS 8
+ns_status ns_profile_enable(int32_t on);
+ns_status ns_profile_read(double* total_ms, int64_t* launches, int32_t n_kinds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NS_H */

@@ -1,0 +1,593 @@
+// ns_api.cpp -- the C ABI of libns.so (include/ns.h).
+//
+// A call validates its arguments on the host (no HIP call before the
+// arguments are known good), plans the batch, makes sure the (device, stream)
+// context holds a large enough workspace, finds or uploads the batch's
+// metadata block, and enqueues the kernel sequence on the caller's stream:
+//
+//   small matrices : k_small (one launch for all of them)
+//   large matrices : norm pieces, norm fold, normalize/transpose/pad, then per
+//                    step the three grouped GEMM stages X X^T, bA + cA^2,
+//                    aX + BX (the last one writes the caller's buffers).
+//
+// Nothing here waits for the device. Workspace growth uses stream-ordered
+// allocation (hipMallocAsync / hipFreeAsync); metadata goes up from pinned
+// host slots that are reused only once their copy has completed (checked with
+// hipEventQuery, never waited on).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/ns.h"
+#include "ns_kernels.h"
+#include "ns_plan.h"
+
+namespace {
+
+using ns::Plan;
+
+thread_local std::string g_last_error;
+
+ns_status fail(ns_status s, const std::string& msg)
+{
+    g_last_error = msg;
+    return s;
+}
+
+ns_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(NS_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// --- profiling --------------------------------------------------------------
+struct ProfRec {
+    int kind;
+    hipEvent_t start, stop;
+};
+
+std::atomic<int> g_prof_on{0};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_pending;
+std::vector<hipEvent_t> g_prof_free;
+double g_prof_ms[ns::kNumKinds];
+int64_t g_prof_n[ns::kNumKinds];
+
+hipEvent_t prof_event()
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_free.empty()) {
+        hipEvent_t e = g_prof_free.back();
+        g_prof_free.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+// --- per (device, stream) context ---------------------------------------------
+struct PinnedSlot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    bool used = false;
+};
+
+struct CachedPlan {
+    std::vector<int64_t> shapes;
+    std::vector<uintptr_t> ptrs;
+    int32_t dtype = 0;
+    void* ws_base = nullptr;
+    void* meta = nullptr;          // device metadata block
+    std::shared_ptr<Plan> plan;
+    uint64_t last_use = 0;
+};
+
+struct Context {
+    std::mutex mu;
+    int device = 0;
+    hipStream_t stream = nullptr;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    std::vector<CachedPlan> plans;
+    std::vector<PinnedSlot> slots;
+    uint64_t clock = 0;
+};
+
+constexpr size_t kMaxCachedPlans = 16;
+constexpr size_t kMaxSlots = 8;
+
+std::mutex g_ctx_mu;
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<Context>> g_ctx;
+
+Context* get_context(int device, hipStream_t stream)
+{
+    std::lock_guard<std::mutex> lk(g_ctx_mu);
+    auto key = std::make_pair(device, reinterpret_cast<uintptr_t>(stream));
+    auto it = g_ctx.find(key);
+    if (it != g_ctx.end())
+        return it->second.get();
+    auto c = std::make_unique<Context>();
+    c->device = device;
+    c->stream = stream;
+    Context* raw = c.get();
+    g_ctx.emplace(key, std::move(c));
+    return raw;
+}
+
+void drop_plans(Context* c)
+{
+    for (CachedPlan& cp : c->plans)
+        if (cp.meta)
+            (void)hipFreeAsync(cp.meta, c->stream);
+    c->plans.clear();
+}
+
+ns_status ensure_workspace(Context* c, size_t bytes)
+{
+    if (bytes <= c->ws_bytes)
+        return NS_OK;
+    // Grow by at least 1/8 to avoid a reallocation per slightly larger batch.
+    size_t want = bytes + bytes / 8;
+    drop_plans(c);  // descriptors point into the old workspace
+    if (c->ws) {
+        hipError_t e = hipFreeAsync(c->ws, c->stream);
+        c->ws = nullptr;
+        c->ws_bytes = 0;
+        if (e != hipSuccess)
+            return hip_fail(e, "hipFreeAsync(workspace)");
+    }
+    hipError_t e = hipMallocAsync(&c->ws, want, c->stream);
+    if (e != hipSuccess) {
+        c->ws = nullptr;
+        (void)hipGetLastError();
+        return fail(NS_ENOMEM, "workspace of " + std::to_string(want) + " bytes: " +
+                                   hipGetErrorString(e));
+    }
+    c->ws_bytes = want;
+    return NS_OK;
+}
+
+// A pinned host slot of at least `bytes` whose previous copy has finished.
+PinnedSlot* get_slot(Context* c, size_t bytes, std::string* err)
+{
+    for (PinnedSlot& s : c->slots) {
+        if (s.cap < bytes)
+            continue;
+        if (!s.used || hipEventQuery(s.done) == hipSuccess)
+            return &s;
+    }
+    if (c->slots.size() >= kMaxSlots) {
+        // Every slot is still in flight: wait for the oldest-sized fitting one.
+        for (PinnedSlot& s : c->slots) {
+            if (s.cap >= bytes) {
+                (void)hipEventSynchronize(s.done);
+                return &s;
+            }
+        }
+    }
+    PinnedSlot s;
+    s.cap = bytes < (1u << 20) ? (1u << 20) : bytes;
+    if (hipHostMalloc(&s.host, s.cap, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        *err = "hipHostMalloc failed";
+        return nullptr;
+    }
+    if (hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        *err = "hipEventCreate failed";
+        return nullptr;
+    }
+    c->slots.push_back(s);
+    return &c->slots.back();
+}
+
+// Host image of the metadata block [0, meta_inv).
+void build_meta(const Plan& p, void* const* ptrs, char* ws, char* meta, std::vector<char>* out)
+{
+    out->assign(p.meta_inv, 0);
+    char* h = out->data();
+    auto ws_at = [&](size_t off) -> void* { return off == SIZE_MAX ? nullptr : ws + off; };
+    for (size_t li = 0; li < p.large.size(); ++li) {
+        const ns::PlanMat& pm = p.mats[p.large[li]];
+        const ns::LargeOffsets& lo = p.large_off[li];
+        ns::LargeMat d{};
+        d.user = ptrs[pm.index];
+        d.rows = pm.rows;
+        d.cols = pm.cols;
+        d.m = pm.m;
+        d.n = pm.n;
+        d.mp = pm.mp;
+        d.np = pm.np;
+        d.trans = pm.trans;
+        d.batch_index = pm.index;
+        d.part_begin = p.part_prefix[li];
+        d.nparts = p.part_prefix[li + 1] - p.part_prefix[li];
+        d.prep_begin = p.prep_prefix[li];
+        d.nprep = p.prep_prefix[li + 1] - p.prep_prefix[li];
+        d.xf = static_cast<float*>(ws_at(lo.xf));
+        for (int s = 0; s < 2; ++s) {
+            d.xb[s] = ws_at(lo.xb[s]);
+            d.xt[s] = ws_at(lo.xt[s]);
+        }
+        d.a = ws_at(lo.a);
+        d.b = ws_at(lo.b);
+        std::memcpy(h + p.meta_large + li * sizeof(ns::LargeMat), &d, sizeof d);
+    }
+    for (size_t si = 0; si < p.small.size(); ++si) {
+        const ns::PlanMat& pm = p.mats[p.small[si]];
+        ns::SmallMat d{};
+        d.user = ptrs[pm.index];
+        d.rows = pm.rows;
+        d.cols = pm.cols;
+        d.m = pm.m;
+        d.n = pm.n;
+        d.trans = pm.trans;
+        d.batch_index = pm.index;
+        d.xw = reinterpret_cast<float*>(ws + p.small_off[si]);
+        std::memcpy(h + p.meta_small + si * sizeof(ns::SmallMat), &d, sizeof d);
+    }
+    if (!p.syrk_tiles.empty())
+        std::memcpy(h + p.meta_syrk, p.syrk_tiles.data(), p.syrk_tiles.size() * sizeof(ns::Tile));
+    if (!p.poly_tiles.empty())
+        std::memcpy(h + p.meta_poly, p.poly_tiles.data(), p.poly_tiles.size() * sizeof(ns::Tile));
+    if (!p.update_tiles.empty())
+        std::memcpy(h + p.meta_update, p.update_tiles.data(), p.update_tiles.size() * sizeof(ns::Tile));
+    std::memcpy(h + p.meta_part_prefix, p.part_prefix.data(), p.part_prefix.size() * sizeof(int32_t));
+    std::memcpy(h + p.meta_prep_prefix, p.prep_prefix.data(), p.prep_prefix.size() * sizeof(int32_t));
+    (void)meta;
+}
+
+bool same_key(const CachedPlan& cp, const int64_t* shapes, void* const* ptrs, int32_t count,
+              int32_t dtype, void* ws)
+{
+    if (cp.dtype != dtype || cp.ws_base != ws || cp.shapes.size() != (size_t)count * 2)
+        return false;
+    if (std::memcmp(cp.shapes.data(), shapes, sizeof(int64_t) * 2 * count) != 0)
+        return false;
+    for (int32_t i = 0; i < count; ++i)
+        if (cp.ptrs[i] != reinterpret_cast<uintptr_t>(ptrs[i]))
+            return false;
+    return true;
+}
+
+// Launch helper: records profiling events around `fn` when profiling is on.
+template <typename F>
+hipError_t timed(int kind, hipStream_t stream, F&& fn)
+{
+    if (!g_prof_on.load(std::memory_order_relaxed))
+        return fn();
+    hipEvent_t a = prof_event(), b = prof_event();
+    if (!a || !b)
+        return fn();
+    (void)hipEventRecord(a, stream);
+    hipError_t e = fn();
+    (void)hipEventRecord(b, stream);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pending.push_back({kind, a, b});
+    return e;
+}
+
+ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t count, int32_t steps,
+              const float* coeffs, int32_t dtype)
+{
+    hipStream_t stream = c->stream;
+    // Plan (or reuse) --------------------------------------------------------
+    CachedPlan* hit = nullptr;
+    for (CachedPlan& cp : c->plans)
+        if (same_key(cp, shapes, ptrs, count, dtype, c->ws)) {
+            hit = &cp;
+            break;
+        }
+    if (!hit) {
+        auto plan = std::make_shared<Plan>();
+        std::string err;
+        int rc = ns::make_plan(shapes, count, dtype, plan.get(), &err);
+        if (rc != 0)
+            return fail((ns_status)rc, err);
+        ns_status st = ensure_workspace(c, plan->data_bytes);
+        if (st != NS_OK)
+            return st;
+        if (c->plans.size() >= kMaxCachedPlans) {
+            size_t lru = 0;
+            for (size_t i = 1; i < c->plans.size(); ++i)
+                if (c->plans[i].last_use < c->plans[lru].last_use)
+                    lru = i;
+            (void)hipFreeAsync(c->plans[lru].meta, stream);
+            c->plans.erase(c->plans.begin() + lru);
+        }
+        CachedPlan cp;
+        cp.shapes.assign(shapes, shapes + 2 * count);
+        cp.ptrs.resize(count);
+        for (int32_t i = 0; i < count; ++i)
+            cp.ptrs[i] = reinterpret_cast<uintptr_t>(ptrs[i]);
+        cp.dtype = dtype;
+        cp.ws_base = c->ws;
+        cp.plan = plan;
+        hipError_t e = hipMallocAsync(&cp.meta, plan->meta_end, stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NS_ENOMEM, std::string("metadata block: ") + hipGetErrorString(e));
+        }
+        std::vector<char> img;
+        build_meta(*plan, ptrs, static_cast<char*>(c->ws), static_cast<char*>(cp.meta), &img);
+        PinnedSlot* slot = get_slot(c, img.size(), &err);
+        if (!slot) {
+            (void)hipFreeAsync(cp.meta, stream);
+            return fail(NS_ENOMEM, err);
+        }
+        std::memcpy(slot->host, img.data(), img.size());
+        e = hipMemcpyAsync(cp.meta, slot->host, img.size(), hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess)
+            e = hipEventRecord(slot->done, stream);
+        slot->used = true;
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(cp.meta, stream);
+            return hip_fail(e, "metadata upload");
+        }
+        c->plans.push_back(std::move(cp));
+        hit = &c->plans.back();
+    }
+    hit->last_use = ++c->clock;
+    const Plan& p = *hit->plan;
+    char* meta = static_cast<char*>(hit->meta);
+    auto* large = reinterpret_cast<const ns::LargeMat*>(meta + p.meta_large);
+    auto* small = reinterpret_cast<const ns::SmallMat*>(meta + p.meta_small);
+    auto* syrk = reinterpret_cast<const ns::Tile*>(meta + p.meta_syrk);
+    auto* poly = reinterpret_cast<const ns::Tile*>(meta + p.meta_poly);
+    auto* upd = reinterpret_cast<const ns::Tile*>(meta + p.meta_update);
+    auto* part_prefix = reinterpret_cast<const int32_t*>(meta + p.meta_part_prefix);
+    auto* prep_prefix = reinterpret_cast<const int32_t*>(meta + p.meta_prep_prefix);
+    auto* inv = reinterpret_cast<float*>(meta + p.meta_inv);
+    auto* partials = reinterpret_cast<float*>(meta + p.meta_partials);
+    const float ca = steps > 0 ? coeffs[0] : 0.f;
+    const float cb = steps > 0 ? coeffs[1] : 0.f;
+    const float cc = steps > 0 ? coeffs[2] : 0.f;
+    const int nl = (int)p.large.size();
+
+    hipError_t e = hipSuccess;
+    if (!p.small.empty()) {
+        e = timed(ns::kKindSmall, stream, [&] {
+            return ns::launch_small(dtype, small, (int)p.small.size(), steps, ca, cb, cc, stream);
+        });
+        if (e != hipSuccess)
+            return hip_fail(e, "small-matrix kernel launch");
+    }
+    if (nl == 0)
+        return NS_OK;
+    e = timed(ns::kKindNormPartial, stream, [&] {
+        return ns::launch_norm_partial(dtype, large, nl, part_prefix, p.total_parts, partials, stream);
+    });
+    if (e == hipSuccess)
+        e = timed(ns::kKindNormFinal, stream, [&] {
+            return ns::launch_norm_final(nl, part_prefix, partials, inv, stream);
+        });
+    if (e != hipSuccess)
+        return hip_fail(e, "norm kernel launch");
+    if (steps == 0) {
+        e = timed(ns::kKindScaleOut, stream, [&] {
+            return ns::launch_scale_out(dtype, large, nl, part_prefix, p.total_parts, inv, stream);
+        });
+        return e == hipSuccess ? NS_OK : hip_fail(e, "scale kernel launch");
+    }
+    e = timed(ns::kKindPrep, stream, [&] {
+        return ns::launch_prep(dtype, large, nl, prep_prefix, p.total_prep, inv, stream);
+    });
+    if (e != hipSuccess)
+        return hip_fail(e, "normalize kernel launch");
+    const int ns_ = (int)p.syrk_tiles.size(), nu = (int)p.update_tiles.size();
+    for (int s = 0; s < steps; ++s) {
+        const int cur = s & 1, last = s == steps - 1;
+        e = timed(ns::kKindSyrk, stream, [&] {
+            return ns::launch_gemm(dtype, 0, large, syrk, ns_, cur, last, ca, cb, cc, stream);
+        });
+        if (e == hipSuccess)
+            e = timed(ns::kKindPoly, stream, [&] {
+                return ns::launch_gemm(dtype, 1, large, poly, ns_, cur, last, ca, cb, cc, stream);
+            });
+        if (e == hipSuccess)
+            e = timed(ns::kKindUpdate, stream, [&] {
+                return ns::launch_gemm(dtype, 2, large, upd, nu, cur, last, ca, cb, cc, stream);
+            });
+        if (e != hipSuccess)
+            return hip_fail(e, "GEMM kernel launch");
+    }
+    return NS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes, int32_t count,
+                                   int32_t steps, const float* coeffs, int32_t dtype, void* stream)
+{
+    g_last_error.clear();
+    if (count < 0)
+        return fail(NS_EINVAL, "count must be >= 0");
+    if (count > 0 && (!ptrs || !shapes))
+        return fail(NS_EINVAL, "ptrs and shapes must not be NULL when count > 0");
+    if (steps < 0)
+        return fail(NS_EINVAL, "steps must be >= 0");
+    if (steps > 0 && !coeffs)
+        return fail(NS_EINVAL, "coeffs must not be NULL when steps > 0");
+    if (dtype != NS_BF16 && dtype != NS_FP32)
+        return fail(NS_EDTYPE, "unknown dtype " + std::to_string(dtype));
+    const size_t elt = dtype == NS_BF16 ? 2 : 4;
+    bool any = false;
+    for (int32_t i = 0; i < count; ++i) {
+        const int64_t r = shapes[2 * i], c = shapes[2 * i + 1];
+        if (r < 0 || c < 0)
+            return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a negative dimension");
+        if (r > (int64_t(1) << 24) || c > (int64_t(1) << 24))
+            return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a dimension above 2^24");
+        if (r == 0 || c == 0)
+            continue;
+        if (!ptrs[i])
+            return fail(NS_EINVAL, "matrix " + std::to_string(i) + " is non-empty but its pointer is NULL");
+        if (reinterpret_cast<uintptr_t>(ptrs[i]) % elt)
+            return fail(NS_EINVAL, "matrix " + std::to_string(i) + " is not aligned to its element size");
+        any = true;
+    }
+    if (!any)
+        return NS_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    Context* c = get_context(dev, static_cast<hipStream_t>(stream));
+    std::lock_guard<std::mutex> lk(c->mu);
+    return run(c, shapes, ptrs, count, steps, coeffs, dtype);
+}
+
+ns_status ns_workspace_bytes(const int64_t* shapes, int32_t count, int32_t dtype, size_t* out_bytes)
+{
+    g_last_error.clear();
+    if (!out_bytes)
+        return fail(NS_EINVAL, "out_bytes is NULL");
+    Plan p;
+    std::string err;
+    int rc = ns::make_plan(shapes, count, dtype, &p, &err);
+    if (rc != 0)
+        return fail((ns_status)rc, err);
+    *out_bytes = p.total_bytes();
+    return NS_OK;
+}
+
+ns_status ns_release_workspace(void* stream)
+{
+    g_last_error.clear();
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::unique_ptr<Context> c;
+    {
+        std::lock_guard<std::mutex> lk(g_ctx_mu);
+        auto it = g_ctx.find(std::make_pair(dev, reinterpret_cast<uintptr_t>(stream)));
+        if (it == g_ctx.end())
+            return NS_OK;
+        c = std::move(it->second);
+        g_ctx.erase(it);
+    }
+    std::lock_guard<std::mutex> lk(c->mu);
+    drop_plans(c.get());
+    if (c->ws)
+        (void)hipFreeAsync(c->ws, c->stream);
+    for (PinnedSlot& s : c->slots) {
+        if (s.used)
+            (void)hipEventSynchronize(s.done);
+        (void)hipEventDestroy(s.done);
+        (void)hipHostFree(s.host);
+    }
+    return NS_OK;
+}
+
+const char* ns_last_error(void) { return g_last_error.c_str(); }
+
+const char* ns_version(void) { return "ns-mi355x 0.1.0 (gfx950)"; }
+
+int64_t ns_compute_cost(int64_t rows, int64_t cols) { return ns::ns_cost(rows, cols); }
+
+ns_status ns_plan_classify(const int64_t* shapes, int32_t count, int32_t dtype, int32_t* kinds)
+{
+    g_last_error.clear();
+    Plan p;
+    std::string err;
+    int rc = ns::make_plan(shapes, count, dtype, &p, &err);
+    if (rc != 0)
+        return fail((ns_status)rc, err);
+    if (count > 0 && !kinds)
+        return fail(NS_EINVAL, "kinds is NULL");
+    for (int32_t i = 0; i < count; ++i)
+        kinds[i] = p.mats[i].cls;
+    return NS_OK;
+}
+
+ns_status ns_plan_tiles(const int64_t* shapes, int32_t count, int32_t dtype, int32_t stage,
+                        int32_t* out, int64_t capacity, int64_t* n_tiles, int32_t* tile_size)
+{
+    g_last_error.clear();
+    if (stage < 0 || stage > 2)
+        return fail(NS_EINVAL, "stage must be 0, 1 or 2");
+    if (!n_tiles || (capacity > 0 && !out) || capacity < 0)
+        return fail(NS_EINVAL, "bad output arguments");
+    Plan p;
+    std::string err;
+    int rc = ns::make_plan(shapes, count, dtype, &p, &err);
+    if (rc != 0)
+        return fail((ns_status)rc, err);
+    const std::vector<ns::Tile>& tl =
+        stage == 2 ? p.update_tiles : stage == 1 ? p.poly_tiles : p.syrk_tiles;
+    *n_tiles = (int64_t)tl.size();
+    if (tile_size)
+        *tile_size = ns::kTile;
+    const int64_t nw = capacity < (int64_t)tl.size() ? capacity : (int64_t)tl.size();
+    for (int64_t i = 0; i < nw; ++i) {
+        const ns::PlanMat& pm = p.mats[p.large[tl[i].mat]];
+        out[4 * i + 0] = pm.index;
+        out[4 * i + 1] = tl[i].bi;
+        out[4 * i + 2] = tl[i].bj;
+        out[4 * i + 3] = stage == 0 ? pm.np : pm.mp;
+    }
+    return NS_OK;
+}
+
+ns_status ns_profile_enable(int32_t on)
+{
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (on) {
+        for (ProfRec& r : g_prof_pending) {
+            g_prof_free.push_back(r.start);
+            g_prof_free.push_back(r.stop);
+        }
+        g_prof_pending.clear();
+        for (int k = 0; k < ns::kNumKinds; ++k) {
+            g_prof_ms[k] = 0.0;
+            g_prof_n[k] = 0;
+        }
+    }
+    g_prof_on.store(on ? 1 : 0);
+    return NS_OK;
+}
+
+ns_status ns_profile_read(double* total_ms, int64_t* launches, int32_t n_kinds)
+{
+    g_last_error.clear();
+    if (n_kinds < 0 || (n_kinds > 0 && (!total_ms || !launches)))
+        return fail(NS_EINVAL, "bad output arguments");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (ProfRec& r : g_prof_pending) {
+        hipError_t e = hipEventSynchronize(r.stop);
+        float ms = 0.f;
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess)
+            return hip_fail(e, "profiling event");
+        g_prof_ms[r.kind] += ms;
+        g_prof_n[r.kind] += 1;
+        g_prof_free.push_back(r.start);
+        g_prof_free.push_back(r.stop);
+    }
+    g_prof_pending.clear();
+    for (int k = 0; k < n_kinds && k < ns::kNumKinds; ++k) {
+        total_ms[k] = g_prof_ms[k];
+        launches[k] = g_prof_n[k];
+    }
+    for (int k = ns::kNumKinds; k < n_kinds; ++k) {
+        total_ms[k] = 0.0;
+        launches[k] = 0;
+    }
+    return NS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// ns_kernels.h -- launch wrappers of the gfx950 kernels (ns_kernels.hip).
+// All launches are asynchronous on `stream`; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ns_internal.h"
+
+namespace ns {
+
+// Fused whole-iteration kernel for matrices with min dim <= kSmallMax, one
+// workgroup per matrix, fp32 arithmetic.
+hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
+                        float a, float b, float c, hipStream_t stream);
+
+// Sum of squares of each large matrix in kNormChunk pieces (one workgroup per
+// piece) ...
+hipError_t launch_norm_partial(int dtype, const LargeMat* mats, int nmats,
+                               const int32_t* part_prefix, int total_parts,
+                               float* partials, hipStream_t stream);
+// ... then one workgroup per matrix folds its pieces into
+// inv[i] = 1 / (sqrt(sum) + 1e-7).
+hipError_t launch_norm_final(int nmats, const int32_t* part_prefix,
+                             const float* partials, float* inv, hipStream_t stream);
+
+// X = G * inv, transposed when rows > cols, zero-padded to mp x np; writes the
+// fp32 master (bf16 path), X and X^T operand copies (slot 0).
+hipError_t launch_prep(int dtype, const LargeMat* mats, int nmats,
+                       const int32_t* prep_prefix, int total_prep,
+                       const float* inv, hipStream_t stream);
+
+// steps == 0: G <- G * inv in place.
+hipError_t launch_scale_out(int dtype, const LargeMat* mats, int nmats,
+                            const int32_t* part_prefix, int total_parts,
+                            const float* inv, hipStream_t stream);
+
+// Grouped GEMM stages over a tile list (one workgroup per 256x256 tile).
+//   stage 0: A = X X^T          (upper-triangle tiles, mirrored)
+//   stage 1: B = b A + c A A    (upper-triangle tiles, mirrored)
+//   stage 2: X <- a X + B X     (all tiles); `last` writes the caller buffer
+// `cur` selects the X operand slot read (the other slot is written).
+hipError_t launch_gemm(int dtype, int stage, const LargeMat* mats,
+                       const Tile* tiles, int ntiles, int cur, int last,
+                       float a, float b, float c, hipStream_t stream);
+
+}  // namespace ns

@@ -1,0 +1,723 @@
+// ns_kernels.hip -- gfx950 (CDNA4) kernels of libns.so.
+//
+// The operation is Muon's quintic Newton-Schulz orthogonalization (see
+// include/ns.h): X = G/(||G||_F + 1e-7), oriented so X is m x n with m <= n,
+// then `steps` times A = X X^T, B = bA + cA^2, X = aX + BX.
+//
+// Kernels:
+//   k_small        whole iteration for min(rows, cols) <= 32, one workgroup per
+//                  matrix, fp32 arithmetic, X kept in an L2-resident buffer.
+//   k_norm_partial sum of squares of a 16K-element piece of G (wave shuffles).
+//   k_norm_final   folds the pieces of a matrix in fixed order -> 1/(||G||+eps).
+//   k_prep         X = G/(||G||+eps), transposed when rows > cols, zero-padded
+//                  to multiples of 256; writes the fp32 master and the X / X^T
+//                  operand copies through a 64x64 LDS tile.
+//   k_gemm<stage>  grouped 256x256 MFMA GEMM over a tile list, C = P Q^T with
+//                  both operands K-contiguous in memory:
+//                    stage 0  P = Q = X            -> A (upper tiles, mirrored)
+//                    stage 1  P = Q = A (= A^T)    -> B = bA + cA^2 (mirrored)
+//                    stage 2  P = B, Q = X^T store -> X = aX + BX
+//   k_scale_out    steps == 0: G <- G/(||G||+eps).
+//
+// Every sum has a fixed order that does not depend on the batch, on the
+// position of a matrix in it, or on trailing zero rows, so a matrix gives the
+// same bits alone or in any batch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ns_kernels.h"
+
+namespace ns {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kEps = 1e-7f;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+// Four consecutive elements from four fp32 values (8-byte bf16 / 16-byte fp32
+// store; the caller guarantees alignment).
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d)
+{
+    bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d)
+{
+    f32x4 v = {a, b, c, d};
+    *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ f32x4 load4(const bf16* p)
+{
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 load4(const float* p)
+{
+    return *reinterpret_cast<const f32x4*>(p);
+}
+
+// Butterfly sum over the 64 lanes of a wavefront (same order on every lane).
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over a 256-thread workgroup in a fixed order; every thread gets it.
+__device__ __forceinline__ float block_sum(float v, float* red4)
+{
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red4[w] = v;
+    __syncthreads();
+    return ((red4[0] + red4[1]) + red4[2]) + red4[3];
+}
+
+// Matrix owning global block `b`: the largest i with prefix[i] <= b.
+__device__ __forceinline__ int find_mat(const int32_t* prefix, int nmats, int b)
+{
+    int lo = 0, hi = nmats - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= b) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Small matrices: m <= 32. One 256-thread workgroup runs the whole iteration.
+//   A = X X^T : 64 threads own a 4x4 block of the 32x32 A each; the four
+//               wavefronts split every 64-column chunk of X by column
+//               (column j of a chunk goes to wavefront j % 4), and the four
+//               partial A's are added in wavefront order.
+//   B = bA + cA^2 in LDS.
+//   X <- aX + BX column by column; thread t owns columns t, t+256, ...
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__ mats,
+                                                    int steps, float ca, float cb, float cc)
+{
+    __shared__ float red[4];
+    __shared__ float xs[64][33];
+    __shared__ float part[4][32][33];
+    __shared__ float as[32][33];
+    __shared__ float bs[32][33];
+
+    const SmallMat S = mats[blockIdx.x];
+    const int tid = threadIdx.x;
+    const int m = S.m, n = S.n;
+    const int64_t cols = S.cols;
+    T* g = static_cast<T*>(S.user);
+    float* xw = S.xw;
+
+    // ||G||_F over G's own row-major order: thread t takes elements t, t+256, ...
+    const int64_t numel = S.rows * S.cols;
+    float s = 0.f;
+    for (int64_t e = tid; e < numel; e += kThreads) {
+        const float v = to_f32(g[e]);
+        s = fmaf(v, v, s);
+    }
+    const float inv = 1.f / (sqrtf(block_sum(s, red)) + kEps);
+
+    for (int e = tid; e < m * n; e += kThreads) {
+        const int i = e / n, j = e - (e / n) * n;
+        const float v = to_f32(S.trans ? g[(int64_t)j * cols + i] : g[(int64_t)i * cols + j]);
+        xw[e] = v * inv;
+    }
+    __syncthreads();
+
+    const int tt = tid & 63, kg = tid >> 6;
+    const int ti = tt >> 3, tj = tt & 7;
+    for (int step = 0; step < steps; ++step) {
+        const bool last = step == steps - 1;
+        float acc[4][4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[p][q] = 0.f;
+        for (int j0 = 0; j0 < n; j0 += 64) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + kThreads * q;
+                const int r = idx >> 6, jj = idx & 63;
+                xs[jj][r] = (r < m && j0 + jj < n) ? xw[r * n + j0 + jj] : 0.f;
+            }
+            __syncthreads();
+            for (int jj = kg; jj < 64; jj += 4) {
+                float xr[4], xc[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    xr[p] = xs[jj][4 * ti + p];
+                    xc[p] = xs[jj][4 * tj + p];
+                }
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[p][q] = fmaf(xr[p], xc[q], acc[p][q]);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                part[kg][4 * ti + p][4 * tj + q] = acc[p][q];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + kThreads * q, r = e >> 5, c = e & 31;
+            as[r][c] = ((part[0][r][c] + part[1][r][c]) + part[2][r][c]) + part[3][r][c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + kThreads * q, r = e >> 5, c = e & 31;
+            float aa = 0.f;
+#pragma unroll
+            for (int t = 0; t < 32; ++t)
+                aa = fmaf(as[r][t], as[t][c], aa);
+            bs[r][c] = cb * as[r][c] + cc * aa;
+        }
+        __syncthreads();
+        for (int j = tid; j < n; j += kThreads) {
+            float x[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r)
+                x[r] = r < m ? xw[r * n + j] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                if (r < m) {
+                    float y = ca * x[r];
+#pragma unroll
+                    for (int t = 0; t < 32; ++t)
+                        y = fmaf(bs[r][t], x[t], y);
+                    if (!last)
+                        xw[r * n + j] = y;
+                    else if (S.trans)
+                        g[(int64_t)j * cols + r] = from_f32<T>(y);
+                    else
+                        g[(int64_t)r * cols + j] = from_f32<T>(y);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (steps == 0) {
+        for (int e = tid; e < m * n; e += kThreads) {
+            const int i = e / n, j = e - (e / n) * n;
+            const int64_t o = S.trans ? (int64_t)j * cols + i : (int64_t)i * cols + j;
+            g[o] = from_f32<T>(xw[e]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Norm, pass 1: one workgroup per kNormChunk elements of G (row-major). Thread
+// t accumulates elements (t + 256 q) * V + e, q outer, e inner, V = 16 bytes
+// of elements; lanes fold by butterfly, wavefronts in order.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_norm_partial(const LargeMat* __restrict__ mats,
+                                                           int nmats,
+                                                           const int32_t* __restrict__ prefix,
+                                                           float* __restrict__ partials)
+{
+    __shared__ float red[4];
+    constexpr int V = 16 / sizeof(T);
+    constexpr int Q = kNormChunk / (kThreads * V);
+    const int b = blockIdx.x;
+    const int mi = find_mat(prefix, nmats, b);
+    const LargeMat& M = mats[mi];
+    const int64_t base = (int64_t)(b - prefix[mi]) * kNormChunk;
+    const int64_t left = M.rows * M.cols - base;
+    const T* g = static_cast<const T*>(M.user) + base;
+    const int tid = threadIdx.x;
+    float s = 0.f;
+    if (left >= kNormChunk && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+        typedef T vec_t __attribute__((ext_vector_type(V)));
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const vec_t v = *reinterpret_cast<const vec_t*>(g + (int64_t)(tid + kThreads * q) * V);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float f = to_f32(v[e]);
+                s = fmaf(f, f, s);
+            }
+        }
+    } else {
+        for (int q = 0; q < Q; ++q) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const int64_t idx = (int64_t)(tid + kThreads * q) * V + e;
+                if (idx < left) {
+                    const float f = to_f32(g[idx]);
+                    s = fmaf(f, f, s);
+                }
+            }
+        }
+    }
+    s = block_sum(s, red);
+    if (tid == 0)
+        partials[b] = s;
+}
+
+// Norm, pass 2: one workgroup per matrix; thread t adds pieces t, t+256, ...
+__global__ __launch_bounds__(kThreads) void k_norm_final(const int32_t* __restrict__ prefix,
+                                                         const float* __restrict__ partials,
+                                                         float* __restrict__ inv)
+{
+    __shared__ float red[4];
+    const int mi = blockIdx.x;
+    const int p0 = prefix[mi], np = prefix[mi + 1] - p0;
+    float s = 0.f;
+    for (int i = threadIdx.x; i < np; i += kThreads)
+        s += partials[p0 + i];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0)
+        inv[mi] = 1.f / (sqrtf(s) + kEps);
+}
+
+// steps == 0: G <- G * inv, same pieces as the norm.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_scale_out(const LargeMat* __restrict__ mats,
+                                                        int nmats,
+                                                        const int32_t* __restrict__ prefix,
+                                                        const float* __restrict__ inv)
+{
+    const int b = blockIdx.x;
+    const int mi = find_mat(prefix, nmats, b);
+    const LargeMat& M = mats[mi];
+    const int64_t base = (int64_t)(b - prefix[mi]) * kNormChunk;
+    const int64_t left = M.rows * M.cols - base;
+    T* g = static_cast<T*>(M.user) + base;
+    const float s = inv[mi];
+    for (int i = threadIdx.x; i < kNormChunk; i += kThreads)
+        if (i < left)
+            g[i] = from_f32<T>(to_f32(g[i]) * s);
+}
+
+// ---------------------------------------------------------------------------
+// Normalize + orient + pad: one workgroup per 64x64 tile of the padded X.
+template <typename T>
+__device__ __forceinline__ void put_x(const LargeMat& M, int64_t i, int64_t j, float v)
+{
+    const int64_t o = i * M.np + j;
+    if (M.xf)
+        M.xf[o] = v;
+    static_cast<T*>(M.xb[0])[o] = from_f32<T>(v);
+}
+template <typename T>
+__device__ __forceinline__ void put_xt(const LargeMat& M, int64_t i, int64_t j, float v)
+{
+    static_cast<T*>(M.xt[0])[j * M.mp + i] = from_f32<T>(v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ mats, int nmats,
+                                                   const int32_t* __restrict__ prefix,
+                                                   const float* __restrict__ inv)
+{
+    __shared__ float tile[kPrepTile][kPrepTile + 1];
+    const int b = blockIdx.x;
+    const int mi = find_mat(prefix, nmats, b);
+    const LargeMat& M = mats[mi];
+    const int local = b - prefix[mi];
+    const int per_row = M.np / kPrepTile;
+    const int64_t i0 = (int64_t)(local / per_row) * kPrepTile;
+    const int64_t j0 = (int64_t)(local % per_row) * kPrepTile;
+    const float s = inv[mi];
+    const T* g = static_cast<const T*>(M.user);
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    if (!M.trans) {
+        // X[i][j] = G[i][j]: read G rows, write X direct, X^T through LDS.
+        for (int p = 0; p < 16; ++p) {
+            const int r = ty + 4 * p;
+            const int64_t i = i0 + r, j = j0 + tx;
+            const float v = (i < M.m && j < M.n) ? to_f32(g[i * M.cols + j]) * s : 0.f;
+            tile[r][tx] = v;
+            put_x<T>(M, i, j, v);
+        }
+        __syncthreads();
+        for (int p = 0; p < 16; ++p) {
+            const int r = ty + 4 * p;
+            put_xt<T>(M, i0 + tx, j0 + r, tile[tx][r]);
+        }
+    } else {
+        // X[i][j] = G[j][i] (G is n x m): read G rows = X columns, write X^T
+        // direct, X through LDS.
+        for (int p = 0; p < 16; ++p) {
+            const int r = ty + 4 * p;
+            const int64_t j = j0 + r, i = i0 + tx;
+            const float v = (i < M.m && j < M.n) ? to_f32(g[j * M.cols + i]) * s : 0.f;
+            tile[r][tx] = v;
+            put_xt<T>(M, i, j, v);
+        }
+        __syncthreads();
+        for (int p = 0; p < 16; ++p) {
+            const int r = ty + 4 * p;
+            put_x<T>(M, i0 + r, j0 + tx, tile[tx][r]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM, C = P Q^T on a 256x256 tile, both operands row-major with K
+// contiguous and leading dimension K. One workgroup of 4 wavefronts (2 x 2),
+// each wavefront 128x128 = 4x4 MFMA blocks of 32x32 (16 fp32 accumulators
+// per lane per block).
+//
+// K advances in k-tiles of 64 bytes per row (32 bf16 / 16 fp32). A k-tile of
+// one operand is 256 rows x 64 B = 16 KB; P and Q k-tiles go through a ring
+// of kStages LDS stages (32 KB each), so kStages-1 k-tiles are in flight while
+// one is multiplied. Global -> LDS moves use buffer_load_dwordx4 ... lds: each
+// lane's 16 bytes land at M0 + 16 * lane, so one wavefront instruction fills
+// 1 KB of LDS, and which global chunk a lane fetches decides the LDS layout.
+//
+// LDS layout of a stage operand: rows r and r+1 (r even) share a 128-byte
+// line L = r/2; logical chunk c (16 B, 0..3) of row r sits at position
+// p = 4*(r & 1) + c of the line, stored at chunk p ^ (L & 7). Eight
+// consecutive rows read at the same logical chunk then hit eight distinct
+// 16-byte bank groups.
+//
+// Lane l of an MFMA operand read takes row (l & 31) of its 32-row block and
+// logical chunk 2*ks + (l >> 5); A and B operands use the same (lane group,
+// element) -> k assignment, so every k meets itself.
+//   bf16: a chunk is 8 values = one v_mfma_f32_32x32x16_bf16.
+//   fp32: a chunk is 4 values = four v_mfma_f32_32x32x2_f32, element e of both
+//         lane groups in MFMA e.
+// Accumulator register r of lane l holds row (r>>2)*8 + (l>>5)*4 + (r&3), column
+// l & 31 of the 32x32 block.
+constexpr int kStageRowBytes = 64;
+constexpr int kStageOpBytes = kTile * kStageRowBytes;   // 16 KB
+constexpr int kStages = 4;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <typename OpT> struct Mfma;
+template <> struct Mfma<bf16> {
+    __device__ static __forceinline__ void mac(f32x16& acc, const uint4& a, const uint4& b)
+    {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+};
+template <> struct Mfma<float> {
+    __device__ static __forceinline__ void mac(f32x16& acc, const uint4& a, const uint4& b)
+    {
+        const f32x4 av = __builtin_bit_cast(f32x4, a), bv = __builtin_bit_cast(f32x4, b);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[0], bv[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[1], bv[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[2], bv[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[3], bv[3], acc, 0, 0, 0);
+    }
+};
+
+// Byte offset of (row r, logical chunk c) inside a stage operand.
+__device__ __forceinline__ int lds_off(int r, int c)
+{
+    const int line = r >> 1;
+    return line * 128 + (((((r & 1) << 2) | c) ^ (line & 7)) << 4);
+}
+
+template <typename OpT, int STAGE>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
+                                                      const Tile* __restrict__ tiles, int cur,
+                                                      int last, float ca, float cb, float cc)
+{
+    // One LDS object per ring stage (P then Q, 16 KB each): with the k loop
+    // unrolled over the ring, every LDS read and every DMA names its stage
+    // statically, so the compiler can see that a refill does not touch the
+    // stage being read and does not wait for it.
+    __shared__ __attribute__((aligned(1024))) char st0[2 * kStageOpBytes];
+    __shared__ __attribute__((aligned(1024))) char st1[2 * kStageOpBytes];
+    __shared__ __attribute__((aligned(1024))) char st2[2 * kStageOpBytes];
+    __shared__ __attribute__((aligned(1024))) char st3[2 * kStageOpBytes];
+
+    const Tile t = tiles[blockIdx.x];
+    const LargeMat& M = mats[t.mat];
+    const char* P;
+    const char* Q;
+    int64_t K;
+    if (STAGE == 0) {
+        P = Q = static_cast<const char*>(M.xb[cur]);
+        K = M.np;
+    } else if (STAGE == 1) {
+        P = Q = static_cast<const char*>(M.a);
+        K = M.mp;
+    } else {
+        P = static_cast<const char*>(M.b);
+        Q = static_cast<const char*>(M.xt[cur]);
+        K = M.mp;
+    }
+    const int ldb = (int)(K * (int64_t)sizeof(OpT));
+    const int nk = ldb / kStageRowBytes;   // a multiple of kStages (K % 256 == 0)
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+
+    // Buffer resources over the 256-row blocks of P and Q (out-of-range reads
+    // would return 0; every offset used below is in range).
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(P + (int64_t)t.bi * kTile * ldb), (short)0, kTile * ldb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Q + (int64_t)t.bj * kTile * ldb), (short)0, kTile * ldb, 0x00020000);
+
+    // DMA mapping: wavefront w fills instructions I = w + 4 q (q = 0..3) of a
+    // stage operand, 1 KB = lines 8I..8I+7 each. Lane l writes line 8I + (l>>3),
+    // stored chunk l & 7, i.e. logical position p = (l & 7) ^ ((l >> 3) & 7):
+    // row 16I + 2 (l >> 3) + (p >> 2), logical chunk p & 3.
+    const int pos = (lane & 7) ^ ((lane >> 3) & 7);
+    const int dma_row = 16 * wave + 2 * (lane >> 3) + (pos >> 2);
+    const int dma_voff = dma_row * ldb + (pos & 3) * 16;
+
+    auto issue = [&](char* sp, int kt) {
+        kt = kt < nk ? kt : nk - 1;   // past the end: reload the last k-tile
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int soff = kt * kStageRowBytes + q * 64 * ldb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rq, (lds_ptr_t)(sp + kStageOpBytes + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    // Fragment offsets (k-step 0) of this lane's rows inside a stage; k-step
+    // 1 is logical chunk 2 + fg, which flips bit 1 of the stored chunk.
+    const int fr = lane & 31, fg = lane >> 5;
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        aoff[i] = lds_off(wr * 128 + i * 32 + fr, fg);
+        boff[i] = kStageOpBytes + lds_off(wc * 128 + i * 32 + fr, fg);
+    }
+    auto compute = [&](const char* sp) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint4 af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = *reinterpret_cast<const uint4*>(sp + (aoff[i] ^ (ks << 5)));
+                bfr[i] = *reinterpret_cast<const uint4*>(sp + (boff[i] ^ (ks << 5)));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Mfma<OpT>::mac(acc[i][j], af[i], bfr[j]);
+        }
+    };
+    // Wait for this wavefront's loads of the oldest pending k-tile (the two
+    // newer ones, 16 loads, may stay in flight) and for every wavefront to
+    // be done with the stage about to be refilled.
+    auto sync_stage = [] {
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    // Prologue: k-tiles 0..2 in flight in stages 0..2.
+    issue(st0, 0);
+    issue(st1, 1);
+    issue(st2, 2);
+    for (int kt = 0; kt < nk; kt += kStages) {
+        sync_stage(); issue(st3, kt + 3); compute(st0);
+        sync_stage(); issue(st0, kt + 4); compute(st1);
+        sync_stage(); issue(st1, kt + 5); compute(st2);
+        sync_stage(); issue(st2, kt + 6); compute(st3);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // Epilogues. Lane l, block (i, j), register group rg holds rows
+    // lr0..lr0+3 of column lc (tile-local).
+    const int64_t gbi = (int64_t)t.bi * kTile, gbj = (int64_t)t.bj * kTile;
+    if (STAGE == 0 || STAGE == 1) {
+        const int64_t ld = M.mp;
+        OpT* out = static_cast<OpT*>(STAGE == 0 ? M.a : M.b);
+        const OpT* ain = static_cast<const OpT*>(M.a);
+        const bool diag = t.bi == t.bj;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int lr0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
+                    const int lc = wc * 128 + j * 32 + fr;
+                    const int64_t r0 = gbi + lr0, c = gbj + lc;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = acc[i][j][rg * 4 + e];
+                    if (STAGE == 1) {
+                        // A is exactly symmetric: A[r0+e][c] = A[c][r0+e].
+                        const f32x4 a4 = load4(ain + c * ld + r0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = cb * a4[e] + cc * v[e];
+                    }
+                    if (!diag) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            out[(r0 + e) * ld + c] = from_f32<OpT>(v[e]);
+                        store4(out + c * ld + r0, v[0], v[1], v[2], v[3]);
+                    } else {
+                        // Diagonal tile: take the upper triangle and mirror it,
+                        // so the stored matrix is exactly symmetric.
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (lr0 + e <= lc)
+                                out[(r0 + e) * ld + c] = from_f32<OpT>(v[e]);
+                            if (lr0 + e < lc)
+                                out[c * ld + r0 + e] = from_f32<OpT>(v[e]);
+                        }
+                    }
+                }
+    } else {
+        const int nxt = cur ^ 1;
+        const int64_t ldx = M.np, ldt = M.mp;
+        const float* xin = M.xf ? M.xf : static_cast<const float*>(M.xb[cur]);
+        float* xf = M.xf;
+        OpT* xb = static_cast<OpT*>(M.xb[nxt]);
+        OpT* xt = static_cast<OpT*>(M.xt[nxt]);
+        OpT* user = static_cast<OpT*>(M.user);
+        // Rows r0..r0+3 of column c: y = a X + (B X).
+        auto group = [&](int64_t r0, int64_t c, float v0, float v1, float v2, float v3) {
+            float y[4] = {v0, v1, v2, v3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                y[e] = fmaf(ca, xin[(r0 + e) * ldx + c], y[e]);
+            if (!last) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (xf)
+                        xf[(r0 + e) * ldx + c] = y[e];
+                    xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
+                }
+                store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
+            } else if (c < M.n) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (r0 + e < M.m) {
+                        const int64_t o = M.trans ? c * M.cols + r0 + e : (r0 + e) * M.cols + c;
+                        user[o] = from_f32<OpT>(y[e]);
+                    }
+                }
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x16 a = acc[i][j];
+                const int64_t r0 = gbi + wr * 128 + i * 32 + fg * 4;
+                const int64_t c = gbj + wc * 128 + j * 32 + fr;
+                group(r0, c, a[0], a[1], a[2], a[3]);
+                group(r0 + 8, c, a[4], a[5], a[6], a[7]);
+                group(r0 + 16, c, a[8], a[9], a[10], a[11]);
+                group(r0 + 24, c, a[12], a[13], a[14], a[15]);
+            }
+    }
+}
+
+template <typename OpT, int STAGE>
+hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, int cur, int last,
+                         float a, float b, float c, hipStream_t stream)
+{
+    hipLaunchKernelGGL((k_gemm<OpT, STAGE>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
+                       cur, last, a, b, c);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps, float a, float b,
+                        float c, hipStream_t stream)
+{
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_small<bf16>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
+    else
+        hipLaunchKernelGGL(k_small<float>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_partial(int dtype, const LargeMat* mats, int nmats, const int32_t* part_prefix,
+                               int total_parts, float* partials, hipStream_t stream)
+{
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_norm_partial<bf16>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+                           nmats, part_prefix, partials);
+    else
+        hipLaunchKernelGGL(k_norm_partial<float>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+                           nmats, part_prefix, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_final(int nmats, const int32_t* part_prefix, const float* partials, float* inv,
+                             hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_norm_final, dim3(nmats), dim3(kThreads), 0, stream, part_prefix, partials, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep(int dtype, const LargeMat* mats, int nmats, const int32_t* prep_prefix,
+                       int total_prep, const float* inv, hipStream_t stream)
+{
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_prep<bf16>, dim3(total_prep), dim3(kThreads), 0, stream, mats, nmats,
+                           prep_prefix, inv);
+    else
+        hipLaunchKernelGGL(k_prep<float>, dim3(total_prep), dim3(kThreads), 0, stream, mats, nmats,
+                           prep_prefix, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_out(int dtype, const LargeMat* mats, int nmats, const int32_t* part_prefix,
+                            int total_parts, const float* inv, hipStream_t stream)
+{
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_scale_out<bf16>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+                           nmats, part_prefix, inv);
+    else
+        hipLaunchKernelGGL(k_scale_out<float>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+                           nmats, part_prefix, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dtype, int stage, const LargeMat* mats, const Tile* tiles, int ntiles,
+                       int cur, int last, float a, float b, float c, hipStream_t stream)
+{
+    if (dtype == 0) {
+        if (stage == 0) return launch_gemm_t<bf16, 0>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+        if (stage == 1) return launch_gemm_t<bf16, 1>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+        return launch_gemm_t<bf16, 2>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+    }
+    if (stage == 0) return launch_gemm_t<float, 0>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+    if (stage == 1) return launch_gemm_t<float, 1>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+    return launch_gemm_t<float, 2>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+}
+
+}  // namespace ns

@@ -1,0 +1,165 @@
+"""C ABI on the CPU: the library loads, exports every declared symbol, rejects
+bad arguments before touching a device, and plans batches as documented.
+No call here reaches the GPU."""
+import itertools
+import os
+import re
+
+import pytest
+
+import newton_schulz_04_amd as ns
+from newton_schulz_04_amd import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ns.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ns_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert "ns_orthogonalize_batched" in names and len(names) >= 10
+    lib = ns.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(ptrs=None, shapes=None, steps=5, count=-1), 1),
+    (dict(ptrs=None, shapes=None, steps=5, count=0), 0),
+    (dict(ptrs=None, shapes=[(4, 4)], steps=5), 1),
+    (dict(ptrs=[0x1000], shapes=None, steps=5, count=1), 1),
+    (dict(ptrs=[0x1000], shapes=[(4, 4)], steps=-1), 1),
+    (dict(ptrs=[0x1000], shapes=[(-1, 4)], steps=5), 1),
+    (dict(ptrs=[0], shapes=[(4, 4)], steps=5), 1),            # NULL for non-empty
+    (dict(ptrs=[0x1001], shapes=[(4, 4)], steps=5), 1),       # misaligned bf16
+    (dict(ptrs=[0x1000], shapes=[(1 << 25, 4)], steps=5), 1),  # too large
+    (dict(ptrs=[0, 0], shapes=[(0, 5), (7, 0)], steps=5), 0),  # empty shards only
+])
+def test_validation_without_device(kwargs, status):
+    kw = dict(coeffs=ns.QUINTIC, dtype=ns.NS_BF16)
+    kw.update(kwargs)
+    rc = ns.orthogonalize_raw(kw["ptrs"], kw["shapes"], kw["steps"], kw["coeffs"],
+                              kw["dtype"], count=kw.get("count"))
+    assert rc == status, ns.last_error()
+    if status:
+        assert ns.last_error()
+
+
+def test_null_coeffs_and_dtype():
+    assert ns.orthogonalize_raw([0x1000], [(4, 4)], 5, None, ns.NS_BF16) == 1
+    assert ns.orthogonalize_raw([0x1000], [(4, 4)], 5, ns.QUINTIC, 9) == 2
+    assert ns.orthogonalize_raw([0x1000], [(0, 4)], 0, None, ns.NS_FP32) == 0
+
+
+def test_cost_model_matches_pages():
+    # Megatron-LM PR #6379, Changes item 1: max(M,N) * min(M,N)^2 ...
+    assert ns.compute_cost(8192, 6144) == 8192 * 6144 ** 2
+    assert ns.compute_cost(6144, 8192) == ns.compute_cost(8192, 6144)
+    # ... Notes: the cost is numel * min(M,N), so numel misranks a matrix by its
+    # aspect factor min(M,N), which spans 512 .. 10240 over that model's shapes.
+    for r, c in workloads.moe_mixed_shapes()[::16]:
+        assert ns.compute_cost(r, c) == r * c * min(r, c)
+    factors = {min(s) for s in workloads.moe_mixed_shapes()}
+    assert min(factors) == 512 and max(factors) == 10240
+    # review thread: the cost pair 268,435,456 vs 16,777,216 (ratio 16)
+    assert ns.compute_cost(1024, 512) == 268435456
+    assert ns.compute_cost(256, 256) == 16777216
+    assert ns.compute_cost(0, 7) == 0 and ns.compute_cost(-1, 3) == -1
+
+
+def test_classification():
+    shapes = [(64, 32), (24, 2304), (33, 1000), (1000, 33), (32, 32), (0, 9), (8192, 6144)]
+    assert ns.plan_classify(shapes, ns.NS_BF16) == [1, 1, 2, 2, 1, 0, 2]
+
+
+def _pad(v, q=256):
+    return -(-v // q) * q
+
+
+@pytest.mark.parametrize("shapes", [
+    [(8192, 6144)] * 2,
+    [(2048, 6144), (512, 10240), (6144, 6144), (300, 520), (520, 300), (24, 2304), (0, 5)],
+])
+def test_tiles_cover_each_block_once(shapes):
+    for stage in (0, 1, 2):
+        tiles, edge = ns.plan_tiles(shapes, ns.NS_BF16, stage)
+        assert edge == 256
+        seen = {}
+        for mat, bi, bj, depth in tiles:
+            r, c = shapes[mat]
+            m, n = min(r, c), max(r, c)
+            assert m > 32
+            assert depth == (_pad(n) if stage == 0 else _pad(m))
+            key = (mat, bi, bj)
+            assert key not in seen
+            seen[key] = True
+        for i, (r, c) in enumerate(shapes):
+            m, n = min(r, c), max(r, c)
+            if r == 0 or c == 0 or m <= 32:
+                continue
+            mb, nb = _pad(m) // 256, _pad(n) // 256
+            want = ({(i, a, b) for a in range(mb) for b in range(a, mb)} if stage < 2 else
+                    {(i, a, b) for a in range(mb) for b in range(nb)})
+            assert {k for k in seen if k[0] == i} == want
+
+
+def _makespan(costs, workers):
+    """Greedy list schedule in list order (the dispatcher's behaviour)."""
+    import heapq
+    heap = [0] * workers
+    for c in costs:
+        t = heapq.heappop(heap)
+        heapq.heappush(heap, t + c)
+    return max(heap)
+
+
+def test_tile_order_is_longest_first_by_cost():
+    shapes = workloads.moe_mixed_shapes()
+    cost = {i: ns.compute_cost(*s) for i, s in enumerate(shapes)}
+    for stage in (0, 1, 2):
+        tiles, _ = ns.plan_tiles(shapes, ns.NS_BF16, stage)
+        depths = [t[3] for t in tiles]
+        assert depths == sorted(depths, reverse=True)
+        for (m1, _, _, d1), (m2, _, _, d2) in zip(tiles, tiles[1:]):
+            if d1 == d2:
+                assert cost[m1] >= cost[m2]
+
+
+def test_lpt_within_graham_bound_bruteforce():
+    # Longest-first list scheduling is within 4/3 - 1/(3W) of optimal.
+    import random
+    rnd = random.Random(0)
+    for _ in range(200):
+        w = rnd.choice([2, 3])
+        jobs = sorted((rnd.randint(1, 20) for _ in range(rnd.randint(2, 8))), reverse=True)
+        opt = min(max(sum(j for j, a in zip(jobs, assign) if a == k) for k in range(w))
+                  for assign in itertools.product(range(w), repeat=len(jobs)))
+        assert _makespan(jobs, w) <= (4 / 3 - 1 / (3 * w)) * opt + 1e-9
+
+
+def test_cost_order_beats_numel_order_on_moe_batch():
+    # The Megatron page's point on one GPU: dispatching work by Newton-Schulz
+    # cost instead of by numel shortens the makespan over the compute units.
+    shapes = workloads.moe_mixed_shapes()
+    tiles, _ = ns.plan_tiles(shapes, ns.NS_BF16, 2)
+    planned = [t[3] for t in tiles]
+    by_numel = sorted(range(len(shapes)), key=lambda i: -shapes[i][0] * shapes[i][1])
+    numel_order = []
+    for i in by_numel:
+        m, n = min(shapes[i]), max(shapes[i])
+        numel_order += [_pad(m)] * ((_pad(m) // 256) * (_pad(n) // 256))
+    assert sorted(planned) == sorted(numel_order)
+    assert _makespan(planned, 256) <= _makespan(numel_order, 256)
+    assert _makespan(planned, 256) <= 1.05 * sum(planned) / 256 + max(planned)
+
+
+def test_workspace_bytes():
+    b = ns.workspace_bytes([(8192, 6144)], ns.NS_BF16)
+    mp, np_ = 6144, 8192
+    data = 4 * mp * np_ + 4 * 2 * mp * np_ + 2 * 2 * mp * mp
+    assert data <= b <= data + (1 << 20)
+    assert ns.workspace_bytes([(0, 3)], ns.NS_BF16) <= 4096   # metadata only

@@ -1,0 +1,188 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs, at sizes the oracle finishes in seconds. Tolerance per
+matrix, relative Frobenius error: 2e-2 for bf16, 1e-4 for fp32; zero rows,
+zero columns and padding must come back as exact +0.0."""
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_04_amd as ns
+from newton_schulz_04_amd import workloads
+from nsutil import TOL, gpu_run, oracle_run, rel_err, zero_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ns.lib()
+
+
+def test_tiny_fp32_workload():
+    cases = workloads.tiny_fp32()
+    out = gpu_run([c.mat for c in cases])
+    for c, y in zip(cases, out):
+        ref = oracle_run(c.mat)
+        e = rel_err(y, ref)
+        assert e <= TOL[torch.float32], e
+    assert zero_bits(out[3][56:])
+    assert out[3][:56].abs().min() > 0
+
+
+def test_attn_gate_workload_padded():
+    cases = workloads.attn_gate()
+    out = gpu_run([c.mat for c in cases])
+    raw_out = gpu_run([c.tags["raw"] for c in cases])
+    for c, y, yr in zip(cases, out, raw_out):
+        real = c.real_rows
+        ref = oracle_run(c.tags["raw"])
+        assert rel_err(y[real], ref) <= TOL[torch.bfloat16]
+        assert zero_bits(y[~real])
+        # zero-row padding leaves the real rows bitwise unchanged
+        assert torch.equal(y[real].view(torch.int16), yr.view(torch.int16))
+
+
+LARGE_SHAPES = [(300, 520), (520, 300), (256, 256), (33, 100), (100, 33), (257, 513),
+                (513, 257), (64, 2000), (700, 1000), (1000, 700), (96, 96)]
+
+
+@pytest.mark.parametrize("shape", LARGE_SHAPES)
+def test_large_bf16_vs_oracle(shape):
+    g = workloads.gaussian(shape, seed=11, index=shape[0] * 7 + shape[1])
+    (y,) = gpu_run([g])
+    e = rel_err(y, oracle_run(g))
+    assert e <= TOL[torch.bfloat16], e
+
+
+@pytest.mark.parametrize("shape", [(300, 520), (520, 300), (64, 100), (257, 300), (40, 40),
+                                   (64, 32), (17, 900)])
+def test_fp32_vs_oracle(shape):
+    g = workloads.gaussian(shape, seed=12, index=shape[0], dtype=torch.float32)
+    (y,) = gpu_run([g])
+    e = rel_err(y, oracle_run(g))
+    assert e <= TOL[torch.float32], e
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(300, 520), (520, 300), (24, 300), (300, 24)])
+def test_zero_rows_and_columns_exact(dtype, shape):
+    g = workloads.gaussian(shape, seed=13, dtype=dtype)
+    g[[0, 7, shape[0] - 1]] = 0
+    g[:, [3, shape[1] - 1]] = 0
+    (y,) = gpu_run([g])
+    assert zero_bits(y[[0, 7, shape[0] - 1]])
+    assert zero_bits(y[:, [3, shape[1] - 1]])
+    assert rel_err(y, oracle_run(g)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_all_zero_matrices(dtype):
+    mats = [torch.zeros(s, dtype=dtype) for s in [(300, 520), (24, 100), (1, 1)]]
+    for y in gpu_run(mats):
+        assert zero_bits(y)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("steps", [0, 1, 2, 3])
+def test_step_counts(dtype, steps):
+    mats = [workloads.gaussian(s, seed=14, index=i, dtype=dtype)
+            for i, s in enumerate([(300, 520), (20, 70), (70, 20)])]
+    out = gpu_run(mats, steps=steps)
+    for g, y in zip(mats, out):
+        assert rel_err(y, oracle_run(g, steps=steps)) <= TOL[dtype]
+
+
+def test_cubic_fp32_reaches_polar_factor():
+    g = workloads.gaussian((200, 300), seed=15, dtype=torch.float32)
+    cubic = (1.5, -0.5, 0.0)
+    (y,) = gpu_run([g], steps=30, coeffs=cubic)
+    assert rel_err(y, oracle_run(g, steps=30, coeffs=cubic)) <= 1e-4
+    u, _, vt = np.linalg.svd(g.double().numpy(), full_matrices=False)
+    assert rel_err(y, u @ vt) <= 1e-4
+
+
+def test_one_by_n_and_scalars():
+    for shape in [(1, 1), (1, 257), (257, 1), (2, 3)]:
+        for dtype in (torch.bfloat16, torch.float32):
+            g = workloads.gaussian(shape, seed=16, dtype=dtype)
+            (y,) = gpu_run([g])
+            assert rel_err(y, oracle_run(g)) <= TOL[dtype]
+
+
+def _mixed_batch(dtype):
+    shapes = [(300, 520), (24, 2304), (0, 17), (520, 300), (64, 32), (33, 40), (9, 0), (256, 1000)]
+    return [workloads.gaussian(s, seed=17, index=i, dtype=dtype) if 0 not in s
+            else torch.zeros(s, dtype=dtype) for i, s in enumerate(shapes)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_batch_results_independent_of_batch(dtype):
+    mats = _mixed_batch(dtype)
+    together = gpu_run(mats)
+    alone = [gpu_run([m])[0] for m in mats]
+    perm = [3, 7, 0, 5, 1, 6, 2, 4]
+    shuffled = gpu_run([mats[i] for i in perm])
+    iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    for i, (a, b) in enumerate(zip(together, alone)):
+        assert a.shape == mats[i].shape
+        assert torch.equal(a.view(iv), b.view(iv)), i
+    for k, i in enumerate(perm):
+        assert torch.equal(shuffled[k].view(iv), together[i].view(iv)), i
+    for g, y in zip(mats, together):
+        if g.numel():
+            assert rel_err(y, oracle_run(g)) <= TOL[dtype]
+
+
+def test_repeated_calls_and_plan_cache():
+    mats = [workloads.gaussian((300, 520), seed=18).cuda(), workloads.gaussian((24, 100), seed=19).cuda()]
+    pristine = [m.clone() for m in mats]
+    ns.orthogonalize(mats)
+    first = [m.clone() for m in mats]
+    for m, p in zip(mats, pristine):
+        m.copy_(p)
+    ns.orthogonalize(mats)                    # same pointers: cached plan
+    for a, b in zip(mats, first):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    other = [workloads.gaussian((700, 300), seed=20).cuda()]
+    ns.orthogonalize(other)                   # different plan in between
+    for m, p in zip(mats, pristine):
+        m.copy_(p)
+    ns.orthogonalize(mats)
+    for a, b in zip(mats, first):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_side_stream_matches_default_stream():
+    g = workloads.gaussian((520, 300), seed=21).cuda()
+    a, b = g.clone(), g.clone()
+    ns.orthogonalize([a])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ns.orthogonalize([b], stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ns.release_workspace(s)
+
+
+def test_contract_errors_leave_buffers_untouched():
+    g = workloads.gaussian((300, 520), seed=22).cuda()
+    before = g.clone()
+    p = g.data_ptr()
+    assert ns.orthogonalize_raw([p, p], [(300, 520), (-1, 3)], 5, ns.QUINTIC, ns.NS_BF16) == 1
+    assert ns.orthogonalize_raw([p], [(300, 520)], 5, ns.QUINTIC, 5) == 2
+    assert ns.orthogonalize_raw([p], [(300, 520)], -2, ns.QUINTIC, ns.NS_BF16) == 1
+    assert ns.orthogonalize_raw([p], [(300, 520)], 5, None, ns.NS_BF16) == 1
+    assert ns.orthogonalize_raw([p, 0], [(300, 520), (0, 4)], 0, None, ns.NS_BF16) == 0
+    torch.cuda.synchronize()
+    # the last call was valid (steps = 0): G / (||G|| + eps)
+    ref = before.float() / (before.float().norm() + 1e-7)
+    assert rel_err(g.cpu(), ref.cpu().double().numpy()) <= 1e-2
+    canary = torch.full((64,), 7.0, device="cuda")
+    assert ns.orthogonalize_raw([canary.data_ptr()], [(0, 64)], 5, ns.QUINTIC, ns.NS_FP32) == 0
+    assert ns.orthogonalize_raw([], [], 5, ns.QUINTIC, ns.NS_FP32) == 0
+    torch.cuda.synchronize()
+    assert bool((canary == 7.0).all())
