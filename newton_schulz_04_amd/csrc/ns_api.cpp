@@ -25,7 +25,7 @@
 #include <utility>
 #include <vector>
 
-#include "../../include/ns.h"
+#include "ns.h"
 #include "ns_kernels.h"
 #include "ns_plan.h"
 
@@ -213,7 +213,7 @@ void build_meta(const Plan& p, void* const* ptrs, char* ws, char* meta, std::vec
         d.nparts = p.part_prefix[li + 1] - p.part_prefix[li];
         d.prep_begin = p.prep_prefix[li];
         d.nprep = p.prep_prefix[li + 1] - p.prep_prefix[li];
-        d.xf = static_cast<float*>(ws_at(lo.xf));
+        d.xft = static_cast<float*>(ws_at(lo.xf));
         for (int s = 0; s < 2; ++s) {
             d.xb[s] = ws_at(lo.xb[s]);
             d.xt[s] = ws_at(lo.xt[s]);

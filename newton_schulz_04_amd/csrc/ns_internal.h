@@ -40,7 +40,7 @@ struct LargeMat {
     int32_t batch_index;
     int32_t part_begin, nparts;   // norm partial sums [part_begin, +nparts)
     int32_t prep_begin, nprep;    // normalize tiles   [prep_begin, +nprep)
-    float* xf;         // fp32 master of X, mp x np (bf16 path only)
+    float* xft;        // fp32 master of X stored transposed, np x mp (bf16 path only)
     void* xb[2];       // X operand copies, mp x np, ping-pong
     void* xt[2];       // X^T operand copies, np x mp, ping-pong
     void* a;           // A = X X^T, mp x mp

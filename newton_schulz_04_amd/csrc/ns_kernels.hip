@@ -10,8 +10,8 @@
 //   k_norm_partial sum of squares of a 16K-element piece of G (wave shuffles).
 //   k_norm_final   folds the pieces of a matrix in fixed order -> 1/(||G||+eps).
 //   k_prep         X = G/(||G||+eps), transposed when rows > cols, zero-padded
-//                  to multiples of 256; writes the fp32 master and the X / X^T
-//                  operand copies through a 64x64 LDS tile.
+//                  to multiples of 256; writes the X / X^T operand copies and
+//                  the fp32 master (stored like X^T) through a 64x64 LDS tile.
 //   k_gemm<stage>  grouped 256x256 MFMA GEMM over a tile list, C = P Q^T with
 //                  both operands K-contiguous in memory:
 //                    stage 0  P = Q = X            -> A (upper tiles, mirrored)
@@ -317,15 +317,15 @@ __global__ __launch_bounds__(kThreads) void k_scale_out(const LargeMat* __restri
 template <typename T>
 __device__ __forceinline__ void put_x(const LargeMat& M, int64_t i, int64_t j, float v)
 {
-    const int64_t o = i * M.np + j;
-    if (M.xf)
-        M.xf[o] = v;
-    static_cast<T*>(M.xb[0])[o] = from_f32<T>(v);
+    static_cast<T*>(M.xb[0])[i * M.np + j] = from_f32<T>(v);
 }
 template <typename T>
 __device__ __forceinline__ void put_xt(const LargeMat& M, int64_t i, int64_t j, float v)
 {
-    static_cast<T*>(M.xt[0])[j * M.mp + i] = from_f32<T>(v);
+    const int64_t o = j * M.mp + i;
+    if (M.xft)
+        M.xft[o] = v;
+    static_cast<T*>(M.xt[0])[o] = from_f32<T>(v);
 }
 
 template <typename T>
@@ -384,16 +384,17 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
 //
 // K advances in k-tiles of 64 bytes per row (32 bf16 / 16 fp32). A k-tile of
 // one operand is 256 rows x 64 B = 16 KB; P and Q k-tiles go through a ring
-// of kStages LDS stages (32 KB each), so kStages-1 k-tiles are in flight while
-// one is multiplied. Global -> LDS moves use buffer_load_dwordx4 ... lds: each
+// of kStages LDS stages (32 KB each): while k-tile kt is multiplied, kt+1 is
+// resident and kt+2, kt+3 are in flight. Global -> LDS moves use buffer_load_dwordx4 ... lds: each
 // lane's 16 bytes land at M0 + 16 * lane, so one wavefront instruction fills
 // 1 KB of LDS, and which global chunk a lane fetches decides the LDS layout.
 //
-// LDS layout of a stage operand: rows r and r+1 (r even) share a 128-byte
-// line L = r/2; logical chunk c (16 B, 0..3) of row r sits at position
-// p = 4*(r & 1) + c of the line, stored at chunk p ^ (L & 7). Eight
-// consecutive rows read at the same logical chunk then hit eight distinct
-// 16-byte bank groups.
+// LDS layout of a stage operand: row r occupies the 64 bytes at r * 64; its
+// logical 16-byte chunk c (0..3) is stored at chunk c ^ g(r), with
+// g(r) = ((r>>1 ^ r>>3) & 1) | ((r>>1) & 2). g is one-to-one on bits {1,2}
+// and on bits {2,3} of r, so the rows an MFMA operand read touches at one
+// logical chunk (8 consecutive rows per 128-byte bank cycle, 16 per
+// 256-byte one) all land on distinct 16-byte bank groups.
 //
 // Lane l of an MFMA operand read takes row (l & 31) of its 32-row block and
 // logical chunk 2*ks + (l >> 5); A and B operands use the same (lane group,
@@ -429,11 +430,8 @@ template <> struct Mfma<float> {
 };
 
 // Byte offset of (row r, logical chunk c) inside a stage operand.
-__device__ __forceinline__ int lds_off(int r, int c)
-{
-    const int line = r >> 1;
-    return line * 128 + (((((r & 1) << 2) | c) ^ (line & 7)) << 4);
-}
+__device__ __forceinline__ int lds_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kStageRowBytes + ((c ^ lds_swz(r)) << 4); }
 
 template <typename OpT, int STAGE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
@@ -479,12 +477,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         (void*)(Q + (int64_t)t.bj * kTile * ldb), (short)0, kTile * ldb, 0x00020000);
 
     // DMA mapping: wavefront w fills instructions I = w + 4 q (q = 0..3) of a
-    // stage operand, 1 KB = lines 8I..8I+7 each. Lane l writes line 8I + (l>>3),
-    // stored chunk l & 7, i.e. logical position p = (l & 7) ^ ((l >> 3) & 7):
-    // row 16I + 2 (l >> 3) + (p >> 2), logical chunk p & 3.
-    const int pos = (lane & 7) ^ ((lane >> 3) & 7);
-    const int dma_row = 16 * wave + 2 * (lane >> 3) + (pos >> 2);
-    const int dma_voff = dma_row * ldb + (pos & 3) * 16;
+    // stage operand, 1 KB = rows 16I..16I+15 each. Lane l writes stored chunk
+    // l & 3 of row 16I + (l >> 2), i.e. logical chunk (l & 3) ^ g(l >> 2).
+    const int dma_row = 16 * wave + (lane >> 2);
+    const int dma_voff = dma_row * ldb + (((lane & 3) ^ lds_swz(lane >> 2)) << 4);
 
     auto issue = [&](char* sp, int kt) {
         kt = kt < nk ? kt : nk - 1;   // past the end: reload the last k-tile
@@ -498,6 +494,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         }
     };
 
+    const int fr = lane & 31, fg = lane >> 5;
+    const int64_t gbi = (int64_t)t.bi * kTile, gbj = (int64_t)t.bj * kTile;
     f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -509,58 +507,99 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
 
     // Fragment offsets (k-step 0) of this lane's rows inside a stage; k-step
     // 1 is logical chunk 2 + fg, which flips bit 1 of the stored chunk.
-    const int fr = lane & 31, fg = lane >> 5;
     int aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         aoff[i] = lds_off(wr * 128 + i * 32 + fr, fg);
         boff[i] = kStageOpBytes + lds_off(wc * 128 + i * 32 + fr, fg);
     }
-    auto compute = [&](const char* sp) {
+    auto read_frags = [&](const char* sp, int ks, uint4 (&af)[4], uint4 (&bfr)[4]) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint4 af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = *reinterpret_cast<const uint4*>(sp + (aoff[i] ^ (ks << 5)));
-                bfr[i] = *reinterpret_cast<const uint4*>(sp + (boff[i] ^ (ks << 5)));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Mfma<OpT>::mac(acc[i][j], af[i], bfr[j]);
+        for (int i = 0; i < 4; ++i) {
+            af[i] = *reinterpret_cast<const uint4*>(sp + (aoff[i] ^ (ks << 5)));
+            bfr[i] = *reinterpret_cast<const uint4*>(sp + (boff[i] ^ (ks << 5)));
         }
     };
-    // Wait for this wavefront's loads of the oldest pending k-tile (the two
-    // newer ones, 16 loads, may stay in flight) and for every wavefront to
-    // be done with the stage about to be refilled.
-    auto sync_stage = [] {
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    auto mfma_block = [&](const uint4 (&af)[4], const uint4 (&bfr)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                Mfma<OpT>::mac(acc[i][j], af[i], bfr[j]);
     };
 
-    // Prologue: k-tiles 0..2 in flight in stages 0..2.
+    // Pipeline. At the top of iteration kt the DMAs of k-tiles kt+1 and kt+2
+    // may be pending; waiting until only kt+2's 8 loads remain and passing
+    // the barrier makes k-tiles kt and kt+1 visible and frees the stage of
+    // kt-1, which is refilled with kt+3. The k-step 0 fragments of kt were
+    // read during iteration kt-1, so MFMAs start right after the barrier; the
+    // k-step 0 fragments of kt+1 are read while kt's MFMAs run.
+    uint4 fa[4], fb[4];
+    auto iteration = [&](const char* cur, const char* nxt, char* refill, int kt) {
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(refill, kt + 3);
+        uint4 a1[4], b1[4];
+        read_frags(cur, 1, a1, b1);
+        mfma_block(fa, fb);
+        read_frags(nxt, 0, fa, fb);
+        mfma_block(a1, b1);
+        // Instruction order for the scheduler: each LDS read and each DMA
+        // issue slots in between two MFMAs, so the matrix pipe never waits
+        // for a whole batch of reads.
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    };
+
     issue(st0, 0);
     issue(st1, 1);
     issue(st2, 2);
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    read_frags(st0, 0, fa, fb);
     for (int kt = 0; kt < nk; kt += kStages) {
-        sync_stage(); issue(st3, kt + 3); compute(st0);
-        sync_stage(); issue(st0, kt + 4); compute(st1);
-        sync_stage(); issue(st1, kt + 5); compute(st2);
-        sync_stage(); issue(st2, kt + 6); compute(st3);
+        iteration(st0, st1, st3, kt);
+        iteration(st1, st2, st0, kt + 1);
+        iteration(st2, st3, st1, kt + 2);
+        iteration(st3, st0, st2, kt + 3);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogues. Lane l, block (i, j), register group rg holds rows
     // lr0..lr0+3 of column lc (tile-local).
-    const int64_t gbi = (int64_t)t.bi * kTile, gbj = (int64_t)t.bj * kTile;
     if (STAGE == 0 || STAGE == 1) {
         const int64_t ld = M.mp;
         OpT* out = static_cast<OpT*>(STAGE == 0 ? M.a : M.b);
         const OpT* ain = static_cast<const OpT*>(M.a);
         const bool diag = t.bi == t.bj;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            // bA + cA^2 needs A at the same places; A is exactly symmetric, so
+            // rows r0..r0+3 of column c are A[c][r0..r0+3], one vector load.
+            // All 16 loads of a block row are issued before any is used.
+            f32x4 a4[4][4];
+            if (STAGE == 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int64_t r0 = gbi + wr * 128 + i * 32 + rg * 8 + fg * 4;
+                        const int64_t c = gbj + wc * 128 + j * 32 + fr;
+                        a4[j][rg] = load4(ain + c * ld + r0);
+                    }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -573,11 +612,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                     for (int e = 0; e < 4; ++e)
                         v[e] = acc[i][j][rg * 4 + e];
                     if (STAGE == 1) {
-                        // A is exactly symmetric: A[r0+e][c] = A[c][r0+e].
-                        const f32x4 a4 = load4(ain + c * ld + r0);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            v[e] = cb * a4[e] + cc * v[e];
+                            v[e] = cb * a4[j][rg][e] + cc * v[e];
                     }
                     if (!diag) {
 #pragma unroll
@@ -596,50 +633,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                         }
                     }
                 }
+        }
     } else {
         const int nxt = cur ^ 1;
         const int64_t ldx = M.np, ldt = M.mp;
-        const float* xin = M.xf ? M.xf : static_cast<const float*>(M.xb[cur]);
-        float* xf = M.xf;
+        // fp32 X before the step, stored like X^T: the bf16 path's master, or
+        // the fp32 path's operand copy (read-only in this launch).
+        const float* src = M.xft ? M.xft : static_cast<const float*>(M.xt[cur]);
+        float* xft = M.xft;
         OpT* xb = static_cast<OpT*>(M.xb[nxt]);
         OpT* xt = static_cast<OpT*>(M.xt[nxt]);
         OpT* user = static_cast<OpT*>(M.user);
-        // Rows r0..r0+3 of column c: y = a X + (B X).
-        auto group = [&](int64_t r0, int64_t c, float v0, float v1, float v2, float v3) {
-            float y[4] = {v0, v1, v2, v3};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                y[e] = fmaf(ca, xin[(r0 + e) * ldx + c], y[e]);
-            if (!last) {
+        for (int i = 0; i < 4; ++i) {
+            // All 16 loads of a block row first (a lane's four rows of a
+            // column are one 16-byte load), then y = aX + BX and the stores.
+            f32x4 xv[4][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (xf)
-                        xf[(r0 + e) * ldx + c] = y[e];
-                    xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int64_t r0 = gbi + wr * 128 + i * 32 + rg * 8 + fg * 4;
+                    const int64_t c = gbj + wc * 128 + j * 32 + fr;
+                    xv[j][rg] = load4(src + c * ldt + r0);
                 }
-                store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
-            } else if (c < M.n) {
+            auto group = [&](int64_t r0, int64_t c, const f32x4& x, float v0, float v1, float v2,
+                             float v3) {
+                float y[4] = {fmaf(ca, x[0], v0), fmaf(ca, x[1], v1), fmaf(ca, x[2], v2),
+                              fmaf(ca, x[3], v3)};
+                if (!last) {
+                    if (xft)
+                        store4(xft + c * ldt + r0, y[0], y[1], y[2], y[3]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (r0 + e < M.m) {
-                        const int64_t o = M.trans ? c * M.cols + r0 + e : (r0 + e) * M.cols + c;
-                        user[o] = from_f32<OpT>(y[e]);
+                    for (int e = 0; e < 4; ++e)
+                        xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
+                    store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
+                } else if (c < M.n) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (r0 + e < M.m) {
+                            const int64_t o = M.trans ? c * M.cols + r0 + e : (r0 + e) * M.cols + c;
+                            user[o] = from_f32<OpT>(y[e]);
+                        }
                     }
                 }
-            }
-        };
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+            };
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f32x16 a = acc[i][j];
                 const int64_t r0 = gbi + wr * 128 + i * 32 + fg * 4;
                 const int64_t c = gbj + wc * 128 + j * 32 + fr;
-                group(r0, c, a[0], a[1], a[2], a[3]);
-                group(r0 + 8, c, a[4], a[5], a[6], a[7]);
-                group(r0 + 16, c, a[8], a[9], a[10], a[11]);
-                group(r0 + 24, c, a[12], a[13], a[14], a[15]);
+                group(r0, c, xv[j][0], a[0], a[1], a[2], a[3]);
+                group(r0 + 8, c, xv[j][1], a[4], a[5], a[6], a[7]);
+                group(r0 + 16, c, xv[j][2], a[8], a[9], a[10], a[11]);
+                group(r0 + 24, c, xv[j][3], a[12], a[13], a[14], a[15]);
             }
+        }
     }
 }
 

@@ -1,14 +1,15 @@
 // ns_plan.cpp -- batch planner for libns.so (host only, no HIP calls).
 //
-// Each matrix is classified (empty / small / large), large matrices are
+// Each matrix is classified (empty / small / large) and large matrices are
 // ordered by the Newton-Schulz cost max(M,N)*min(M,N)^2 (NVIDIA/Megatron-LM
 // PR #6379, "Balance LayerWise optimizer shards by Newton-Schulz cost, not
 // parameter size", Changes items 1-2: order and assign by that cost, largest
-// first), and every grouped GEMM stage gets one tile list for the whole
-// batch. Tiles are sorted by their own work (K depth x 256^2) largest first,
-// ties keeping the cost order of their matrices, so the hardware dispatcher,
+// first). Every grouped GEMM stage gets one tile list for the whole batch:
+// tiles are grouped per XCD so that the compute units sharing an L2 work on
+// neighbouring tiles, and groups go longest first (K depth x 256^2, then the
+// cost order of their matrices) to the least-loaded XCD, so the dispatcher,
 // which hands out workgroups in index order as compute units free up, runs a
-// longest-processing-time-first list schedule over all compute units.
+// longest-processing-time-first list schedule.
 #include "ns_plan.h"
 
 #include <algorithm>
@@ -19,11 +20,77 @@ namespace ns {
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;
+// Dispatch topology: XCDs per device and the tile group one XCD runs at once.
+constexpr int kXcds = 8;
+constexpr int kGroupRows = 4, kGroupCols = 8;
+enum { kStageSyrk = 0, kStagePoly = 1, kStageUpdate = 2 };
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int32_t pad_to(int64_t v, int64_t q) { return (int32_t)((v + q - 1) / q * q); }
+
+// Tile order of one grouped GEMM stage.
+//
+// The dispatcher hands workgroup w to XCD w % kXcds, and each XCD's 32 compute
+// units share one L2. So the list is built per XCD: every matrix's tile grid
+// is cut into groups of kGroupRows x kGroupCols tiles (one group = what an
+// XCD's compute units run at once, sharing kGroupRows + kGroupCols operand
+// blocks), groups are taken longest first (K depth, then the cost order of
+// their matrices), each goes to the XCD with the least work so far, and the
+// XCD sequences are interleaved so that position w holds the next tile of XCD
+// w % kXcds. An XCD that runs out early takes the next tile of the XCD with
+// the most work left.
+std::vector<Tile> order_tiles(const Plan& p, int stage)
+{
+    struct Group { int64_t depth; std::vector<Tile> tiles; };
+    std::vector<Group> groups;
+    for (size_t li = 0; li < p.large.size(); ++li) {
+        const PlanMat& pm = p.mats[p.large[li]];
+        const int mb = pm.mp / kTile;
+        const int nb = stage == kStageUpdate ? pm.np / kTile : mb;
+        const int64_t depth = stage == kStageSyrk ? pm.np : pm.mp;
+        for (int gi = 0; gi < mb; gi += kGroupRows)
+            for (int gj = 0; gj < nb; gj += kGroupCols) {
+                Group g{depth, {}};
+                for (int bi = gi; bi < std::min(gi + kGroupRows, mb); ++bi)
+                    for (int bj = gj; bj < std::min(gj + kGroupCols, nb); ++bj)
+                        if (stage == kStageUpdate || bj >= bi)
+                            g.tiles.push_back(Tile{(int32_t)li, (int16_t)bi, (int16_t)bj});
+                if (!g.tiles.empty())
+                    groups.push_back(std::move(g));
+            }
+    }
+    std::stable_sort(groups.begin(), groups.end(),
+                     [](const Group& a, const Group& b) { return a.depth > b.depth; });
+    std::vector<std::vector<Tile>> xcd(kXcds);
+    std::vector<int64_t> load(kXcds, 0);
+    size_t total = 0;
+    for (const Group& g : groups) {
+        int best = 0;
+        for (int x = 1; x < kXcds; ++x)
+            if (load[x] < load[best]) best = x;
+        load[best] += g.depth * (int64_t)g.tiles.size();
+        xcd[best].insert(xcd[best].end(), g.tiles.begin(), g.tiles.end());
+        total += g.tiles.size();
+    }
+    std::vector<Tile> out;
+    out.reserve(total);
+    std::vector<size_t> next(kXcds, 0);
+    for (size_t pos = 0; pos < total; ++pos) {
+        int x = (int)(pos % kXcds);
+        if (next[x] == xcd[x].size()) {
+            int most = -1;
+            for (int y = 0; y < kXcds; ++y)
+                if (next[y] < xcd[y].size() &&
+                    (most < 0 || xcd[y].size() - next[y] > xcd[most].size() - next[most]))
+                    most = y;
+            x = most;
+        }
+        out.push_back(xcd[x][next[x]++]);
+    }
+    return out;
+}
 
 }  // namespace
 
@@ -101,22 +168,11 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
     std::stable_sort(p.large.begin(), p.large.end(), by_cost);
     std::stable_sort(p.small.begin(), p.small.end(), by_cost);
 
-    // Tile lists. Within a matrix, tiles run row by row.
-    struct Item { Tile t; int64_t depth; };
-    std::vector<Item> syrk, poly, upd;
+    // Tile lists. Norm and normalize pieces per matrix first.
     p.part_prefix.assign(1, 0);
     p.prep_prefix.assign(1, 0);
     for (size_t li = 0; li < p.large.size(); ++li) {
         const PlanMat& pm = p.mats[p.large[li]];
-        const int mb = pm.mp / kTile, nb = pm.np / kTile;
-        for (int bi = 0; bi < mb; ++bi)
-            for (int bj = bi; bj < mb; ++bj) {
-                syrk.push_back({Tile{(int32_t)li, (int16_t)bi, (int16_t)bj}, pm.np});
-                poly.push_back({Tile{(int32_t)li, (int16_t)bi, (int16_t)bj}, pm.mp});
-            }
-        for (int bi = 0; bi < mb; ++bi)
-            for (int bj = 0; bj < nb; ++bj)
-                upd.push_back({Tile{(int32_t)li, (int16_t)bi, (int16_t)bj}, pm.mp});
         const int64_t numel = pm.rows * pm.cols;
         const int64_t parts = (numel + kNormChunk - 1) / kNormChunk;
         const int64_t prep = (int64_t)(pm.mp / kPrepTile) * (pm.np / kPrepTile);
@@ -128,13 +184,9 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
         p.part_prefix.push_back(p.part_prefix.back() + (int32_t)parts);
         p.prep_prefix.push_back(p.prep_prefix.back() + (int32_t)prep);
     }
-    auto by_depth = [](const Item& a, const Item& b) { return a.depth > b.depth; };
-    std::stable_sort(syrk.begin(), syrk.end(), by_depth);
-    std::stable_sort(poly.begin(), poly.end(), by_depth);
-    std::stable_sort(upd.begin(), upd.end(), by_depth);
-    for (const Item& it : syrk) p.syrk_tiles.push_back(it.t);
-    for (const Item& it : poly) p.poly_tiles.push_back(it.t);
-    for (const Item& it : upd) p.update_tiles.push_back(it.t);
+    p.syrk_tiles = order_tiles(p, kStageSyrk);
+    p.poly_tiles = order_tiles(p, kStagePoly);
+    p.update_tiles = order_tiles(p, kStageUpdate);
     p.total_parts = p.part_prefix.back();
     p.total_prep = p.prep_prefix.back();
 

@@ -117,16 +117,38 @@ def _makespan(costs, workers):
     return max(heap)
 
 
-def test_tile_order_is_longest_first_by_cost():
+def test_tile_order_is_longest_first_per_xcd():
+    # Workgroup w runs on XCD w % 8: each XCD's sequence is longest first
+    # (a few tail tiles taken over from busier XCDs excepted), and within one
+    # K depth, matrices go in cost order.
     shapes = workloads.moe_mixed_shapes()
     cost = {i: ns.compute_cost(*s) for i, s in enumerate(shapes)}
     for stage in (0, 1, 2):
         tiles, _ = ns.plan_tiles(shapes, ns.NS_BF16, stage)
-        depths = [t[3] for t in tiles]
-        assert depths == sorted(depths, reverse=True)
-        for (m1, _, _, d1), (m2, _, _, d2) in zip(tiles, tiles[1:]):
-            if d1 == d2:
-                assert cost[m1] >= cost[m2]
+        for x in range(8):
+            seq = tiles[x::8]
+            head = seq[: int(0.9 * len(seq))]
+            depths = [t[3] for t in head]
+            assert depths == sorted(depths, reverse=True)
+            first = {}
+            for m, _, _, d in head:
+                first.setdefault(d, []).append(m)
+            for d, ms in first.items():
+                order = list(dict.fromkeys(ms))
+                assert [cost[m] for m in order] == sorted((cost[m] for m in order), reverse=True)
+
+
+@pytest.mark.parametrize("stage", [0, 2])
+def test_xcd_groups_share_operands(stage):
+    # The 32 tiles an XCD runs at once touch few operand blocks (L2 reuse).
+    tiles, _ = ns.plan_tiles([(8192, 6144)] * 8, ns.NS_BF16, stage)
+    for x in range(8):
+        first = tiles[x::8][:32]
+        if stage == 0:   # both operands are row blocks of the same X
+            blocks = {(m, bi) for m, bi, _, _ in first} | {(m, bj) for m, _, bj, _ in first}
+        else:            # row blocks of B, row blocks of X^T
+            blocks = {(m, bi) for m, bi, _, _ in first} | {(m, 100 + bj) for m, _, bj, _ in first}
+        assert len(blocks) <= 16
 
 
 def test_lpt_within_graham_bound_bruteforce():
