@@ -207,6 +207,9 @@ void build_meta(const Plan& p, void* const* ptrs, char* ws, char* meta, std::vec
         d.n = pm.n;
         d.mp = pm.mp;
         d.np = pm.np;
+        d.ldx = pm.ldx;
+        d.ldt = pm.ldt;
+        d.ldf = pm.ldf;
         d.trans = pm.trans;
         d.batch_index = pm.index;
         d.part_begin = p.part_prefix[li];

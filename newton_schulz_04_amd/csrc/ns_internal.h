@@ -36,6 +36,9 @@ struct LargeMat {
     int64_t rows, cols;
     int32_t m, n;      // oriented dims
     int32_t mp, np;    // padded dims
+    int32_t ldx;       // row pitch (elements) of xb: rows of np
+    int32_t ldt;       // row pitch (elements) of xt, a, b: rows of mp
+    int32_t ldf;       // row pitch (elements) of xft: rows of mp fp32
     int32_t trans;     // 1 when rows > cols (X = G^T)
     int32_t batch_index;
     int32_t part_begin, nparts;   // norm partial sums [part_begin, +nparts)

@@ -317,15 +317,15 @@ __global__ __launch_bounds__(kThreads) void k_scale_out(const LargeMat* __restri
 template <typename T>
 __device__ __forceinline__ void put_x(const LargeMat& M, int64_t i, int64_t j, float v)
 {
-    static_cast<T*>(M.xb[0])[i * M.np + j] = from_f32<T>(v);
+    if (M.xb[0])
+        static_cast<T*>(M.xb[0])[i * M.ldx + j] = from_f32<T>(v);
 }
 template <typename T>
 __device__ __forceinline__ void put_xt(const LargeMat& M, int64_t i, int64_t j, float v)
 {
-    const int64_t o = j * M.mp + i;
     if (M.xft)
-        M.xft[o] = v;
-    static_cast<T*>(M.xt[0])[o] = from_f32<T>(v);
+        M.xft[j * M.ldf + i] = v;
+    static_cast<T*>(M.xt[0])[j * M.ldt + i] = from_f32<T>(v);
 }
 
 template <typename T>
@@ -382,19 +382,19 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
 // each wavefront 128x128 = 4x4 MFMA blocks of 32x32 (16 fp32 accumulators
 // per lane per block).
 //
-// K advances in k-tiles of 64 bytes per row (32 bf16 / 16 fp32). A k-tile of
-// one operand is 256 rows x 64 B = 16 KB; P and Q k-tiles go through a ring
-// of kStages LDS stages (32 KB each): while k-tile kt is multiplied, kt+1 is
-// resident and kt+2, kt+3 are in flight. Global -> LDS moves use buffer_load_dwordx4 ... lds: each
+// K advances in k-tiles of 128 bytes per row (64 bf16 / 32 fp32). A k-tile of
+// one operand is 256 rows x 128 B = 32 KB; P and Q k-tiles alternate between
+// two LDS stages (64 KB each): while k-tile kt is multiplied, kt+1 streams
+// into the other stage. Global -> LDS moves use buffer_load_dwordx4 ... lds: each
 // lane's 16 bytes land at M0 + 16 * lane, so one wavefront instruction fills
 // 1 KB of LDS, and which global chunk a lane fetches decides the LDS layout.
 //
-// LDS layout of a stage operand: row r occupies the 64 bytes at r * 64; its
-// logical 16-byte chunk c (0..3) is stored at chunk c ^ g(r), with
-// g(r) = ((r>>1 ^ r>>3) & 1) | ((r>>1) & 2). g is one-to-one on bits {1,2}
-// and on bits {2,3} of r, so the rows an MFMA operand read touches at one
-// logical chunk (8 consecutive rows per 128-byte bank cycle, 16 per
-// 256-byte one) all land on distinct 16-byte bank groups.
+// LDS layout of a stage operand: row r occupies the 128 bytes at r * 128; its
+// logical 16-byte chunk c (0..7) is stored at chunk c ^ g(r), with
+// g(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7. Over any 8 consecutive rows g takes
+// 8 distinct values, and over 16 it takes 8 distinct values per row parity,
+// so the rows an MFMA operand read touches at one logical chunk (8 per
+// 128-byte bank cycle, 16 per 256-byte one) land on distinct bank groups.
 //
 // Lane l of an MFMA operand read takes row (l & 31) of its 32-row block and
 // logical chunk 2*ks + (l >> 5); A and B operands use the same (lane group,
@@ -404,9 +404,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
 //         lane groups in MFMA e.
 // Accumulator register r of lane l holds row (r>>2)*8 + (l>>5)*4 + (r&3), column
 // l & 31 of the 32x32 block.
-constexpr int kStageRowBytes = 64;
-constexpr int kStageOpBytes = kTile * kStageRowBytes;   // 16 KB
-constexpr int kStages = 4;
+constexpr int kStageRowBytes = 128;
+constexpr int kStageOpBytes = kTile * kStageRowBytes;   // 32 KB
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -430,63 +429,103 @@ template <> struct Mfma<float> {
 };
 
 // Byte offset of (row r, logical chunk c) inside a stage operand.
-__device__ __forceinline__ int lds_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kStageRowBytes + ((c ^ lds_swz(r)) << 4); }
+
+// X X^T on the bf16 path reads X from its transposed copy X^T (np x mp), so
+// no row-major copy of X is kept. A k-tile of an operand is then 64 rows of
+// X^T (64 k) x 256 columns (256 rows of X): 64 LDS rows of 512 bytes, the
+// 16-byte chunk c of row k stored at chunk c ^ ((k & 3) << 2).
+//
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, the 16 8-byte
+// chunks the lanes address form a 4 x 16 matrix of 16-bit values (row r =
+// the chunks of lanes 4r..4r+3) and lane j receives column j. Lane x of a
+// group addressing row k0 + x/4, columns i0 + 4 (x % 4) .. +3 of the k-tile
+// therefore receives the four values at rows k0..k0+3 of column i0 + x:
+// four consecutive k of one row of X, half an MFMA operand.
+template <typename T> struct IsBf16 { static constexpr bool value = false; };
+template <> struct IsBf16<bf16> { static constexpr bool value = true; };
+constexpr int kTrRowBytes = 512;
+__device__ __forceinline__ int tr_swz(int k) { return (k & 3) << 2; }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ds_read_tr(const char* p)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p)));
+}
 
 template <typename OpT, int STAGE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
                                                       const Tile* __restrict__ tiles, int cur,
                                                       int last, float ca, float cb, float cc)
 {
-    // One LDS object per ring stage (P then Q, 16 KB each): with the k loop
-    // unrolled over the ring, every LDS read and every DMA names its stage
+    // Two LDS stages (P then Q, 32 KB each), one object each: with the k loop
+    // unrolled over both, every LDS read and every DMA names its stage
     // statically, so the compiler can see that a refill does not touch the
     // stage being read and does not wait for it.
     __shared__ __attribute__((aligned(1024))) char st0[2 * kStageOpBytes];
     __shared__ __attribute__((aligned(1024))) char st1[2 * kStageOpBytes];
-    __shared__ __attribute__((aligned(1024))) char st2[2 * kStageOpBytes];
-    __shared__ __attribute__((aligned(1024))) char st3[2 * kStageOpBytes];
 
     const Tile t = tiles[blockIdx.x];
     const LargeMat& M = mats[t.mat];
     const char* P;
     const char* Q;
-    int64_t K;
-    if (STAGE == 0) {
+    constexpr bool kTrans = STAGE == 0 && IsBf16<OpT>::value;
+    int64_t K, pitch;
+    if (kTrans) {
+        P = Q = static_cast<const char*>(M.xt[cur]);
+        K = M.np;
+        pitch = M.ldt;
+    } else if (STAGE == 0) {
         P = Q = static_cast<const char*>(M.xb[cur]);
         K = M.np;
+        pitch = M.ldx;
     } else if (STAGE == 1) {
         P = Q = static_cast<const char*>(M.a);
         K = M.mp;
+        pitch = M.ldt;
     } else {
         P = static_cast<const char*>(M.b);
         Q = static_cast<const char*>(M.xt[cur]);
         K = M.mp;
+        pitch = M.ldt;
     }
-    const int ldb = (int)(K * (int64_t)sizeof(OpT));
-    const int nk = ldb / kStageRowBytes;   // a multiple of kStages (K % 256 == 0)
+    const int ldb = (int)(pitch * (int64_t)sizeof(OpT));        // row pitch, bytes
+    // k-tiles: 128 bytes of K per row, or 64 rows of X^T (the same 64 bf16)
+    const int nk = (int)(K * (int64_t)sizeof(OpT) / kStageRowBytes);   // even (K % 256 == 0)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
 
     // Buffer resources over the 256-row blocks of P and Q (out-of-range reads
     // would return 0; every offset used below is in range).
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(P + (int64_t)t.bi * kTile * ldb), (short)0, kTile * ldb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Q + (int64_t)t.bj * kTile * ldb), (short)0, kTile * ldb, 0x00020000);
+    // (Transposed operands: the blocks are column ranges of X^T and the
+    // resource spans all np rows.)
+    const int64_t poff = kTrans ? (int64_t)t.bi * kTile * 2 : (int64_t)t.bi * kTile * ldb;
+    const int64_t qoff = kTrans ? (int64_t)t.bj * kTile * 2 : (int64_t)t.bj * kTile * ldb;
+    const int range_p = kTrans ? (int)((int64_t)M.np * ldb - poff) : kTile * ldb;
+    const int range_q = kTrans ? (int)((int64_t)M.np * ldb - qoff) : kTile * ldb;
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(P + poff), (short)0, range_p, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + qoff), (short)0, range_q, 0x00020000);
 
-    // DMA mapping: wavefront w fills instructions I = w + 4 q (q = 0..3) of a
-    // stage operand, 1 KB = rows 16I..16I+15 each. Lane l writes stored chunk
-    // l & 3 of row 16I + (l >> 2), i.e. logical chunk (l & 3) ^ g(l >> 2).
-    const int dma_row = 16 * wave + (lane >> 2);
-    const int dma_voff = dma_row * ldb + (((lane & 3) ^ lds_swz(lane >> 2)) << 4);
+    // DMA mapping: wavefront w fills instructions I = w + 4 q (q = 0..7) of a
+    // stage operand, 1 KB = rows 8I..8I+7 each. Lane l writes stored chunk
+    // l & 7 of row 8I + (l >> 3), i.e. logical chunk (l & 7) ^ g(row); the
+    // q offset (32 rows) leaves g unchanged.
+    // Transposed: instruction I fills LDS rows 2I, 2I+1 (k); lane l writes
+    // stored chunk l & 31 of row 2I + (l >> 5); the q offset (8 rows) leaves
+    // the swizzle unchanged.
+    const int dma_row = kTrans ? 2 * wave + (lane >> 5) : 8 * wave + (lane >> 3);
+    const int dma_voff = kTrans ? dma_row * ldb + (((lane & 31) ^ tr_swz(dma_row)) << 4)
+                                : dma_row * ldb + (((lane & 7) ^ lds_swz(dma_row)) << 4);
 
     auto issue = [&](char* sp, int kt) {
         kt = kt < nk ? kt : nk - 1;   // past the end: reload the last k-tile
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int soff = kt * kStageRowBytes + q * 64 * ldb;
+        for (int q = 0; q < 8; ++q) {
+            const int soff = kTrans ? (kt * 64 + 8 * q) * ldb : kt * kStageRowBytes + q * 32 * ldb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -506,18 +545,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                 acc[i][j][r] = 0.f;
 
     // Fragment offsets (k-step 0) of this lane's rows inside a stage; k-step
-    // 1 is logical chunk 2 + fg, which flips bit 1 of the stored chunk.
+    // ks is logical chunk 2 ks + fg, which XORs the stored chunk with 2 ks.
+    // Transposed: lane l (group g = l >> 4, x = l & 15) reads row
+    // ks*16 + 8 (g >> 1) + 4 e + (x >> 2), columns base + 16 (g & 1) + 4 (x & 3);
+    // k-step ks and half e only add whole rows (ks * 8192 + e * 2048 bytes).
     int aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        aoff[i] = lds_off(wr * 128 + i * 32 + fr, fg);
-        boff[i] = kStageOpBytes + lds_off(wc * 128 + i * 32 + fr, fg);
+        if (kTrans) {
+            const int g = lane >> 4, x = lane & 15;
+            const int kr = 8 * (g >> 1) + (x >> 2);
+            const int ca = wr * 128 + i * 32 + 16 * (g & 1) + 4 * (x & 3);
+            const int cb = wc * 128 + i * 32 + 16 * (g & 1) + 4 * (x & 3);
+            aoff[i] = kr * kTrRowBytes + (((ca >> 3) ^ tr_swz(kr)) << 4) + (ca & 7) * 2;
+            boff[i] = kStageOpBytes + kr * kTrRowBytes + (((cb >> 3) ^ tr_swz(kr)) << 4) + (cb & 7) * 2;
+        } else {
+            aoff[i] = lds_off(wr * 128 + i * 32 + fr, fg);
+            boff[i] = kStageOpBytes + lds_off(wc * 128 + i * 32 + fr, fg);
+        }
     }
     auto read_frags = [&](const char* sp, int ks, uint4 (&af)[4], uint4 (&bfr)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            af[i] = *reinterpret_cast<const uint4*>(sp + (aoff[i] ^ (ks << 5)));
-            bfr[i] = *reinterpret_cast<const uint4*>(sp + (boff[i] ^ (ks << 5)));
+            if (kTrans) {
+                const uint2 a0 = ds_read_tr(sp + aoff[i] + ks * 8192);
+                const uint2 a1 = ds_read_tr(sp + aoff[i] + ks * 8192 + 2048);
+                const uint2 b0 = ds_read_tr(sp + boff[i] + ks * 8192);
+                const uint2 b1 = ds_read_tr(sp + boff[i] + ks * 8192 + 2048);
+                af[i] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+                bfr[i] = make_uint4(b0.x, b0.y, b1.x, b1.y);
+            } else {
+                af[i] = *reinterpret_cast<const uint4*>(sp + (aoff[i] ^ (ks << 5)));
+                bfr[i] = *reinterpret_cast<const uint4*>(sp + (boff[i] ^ (ks << 5)));
+            }
         }
     };
     auto mfma_block = [&](const uint4 (&af)[4], const uint4 (&bfr)[4]) {
@@ -527,60 +587,58 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             for (int j = 0; j < 4; ++j)
                 Mfma<OpT>::mac(acc[i][j], af[i], bfr[j]);
     };
-
-    // Pipeline. At the top of iteration kt the DMAs of k-tiles kt+1 and kt+2
-    // may be pending; waiting until only kt+2's 8 loads remain and passing
-    // the barrier makes k-tiles kt and kt+1 visible and frees the stage of
-    // kt-1, which is refilled with kt+3. The k-step 0 fragments of kt were
-    // read during iteration kt-1, so MFMAs start right after the barrier; the
-    // k-step 0 fragments of kt+1 are read while kt's MFMAs run.
-    uint4 fa[4], fb[4];
-    auto iteration = [&](const char* cur, const char* nxt, char* refill, int kt) {
-        asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        issue(refill, kt + 3);
-        uint4 a1[4], b1[4];
-        read_frags(cur, 1, a1, b1);
-        mfma_block(fa, fb);
-        read_frags(nxt, 0, fa, fb);
-        mfma_block(a1, b1);
-        // Instruction order for the scheduler: each LDS read and each DMA
-        // issue slots in between two MFMAs, so the matrix pipe never waits
-        // for a whole batch of reads.
+    auto interleave = [] {
+        // LDS reads spread between MFMAs (16 transposed 8-byte reads or 8
+        // 16-byte reads per k-step)
+        constexpr int nreads = kTrans ? 16 : 8;
+        constexpr int per = kTrans ? 1 : 1;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < nreads; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        if (!kTrans)
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    };
+
+    // Pipeline over two stages. Iteration kt multiplies stage `cur` (k-tile
+    // kt) while the DMA of k-tile kt+1 fills `oth`, freed by the barrier that
+    // ended iteration kt-1. Each k-step's fragments are read while the
+    // previous k-step's MFMAs run; after the last read of `cur`, the wave
+    // waits for its own DMA and passes the barrier (so `oth` is complete and
+    // nobody reads `cur` any more), reads k-step 0 of `oth` and issues the
+    // last k-step's MFMAs to cover that read.
+    uint4 fa[4], fb[4], ga[4], gb[4];
+    auto iteration = [&](const char* cur, char* oth, int kt) {
+        issue(oth, kt + 1);
+        read_frags(cur, 1, ga, gb);
+        mfma_block(fa, fb);
+        interleave();
+        read_frags(cur, 2, fa, fb);
+        mfma_block(ga, gb);
+        interleave();
+        read_frags(cur, 3, ga, gb);
+        mfma_block(fa, fb);
+        interleave();
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        read_frags(oth, 0, fa, fb);
+        mfma_block(ga, gb);
+        interleave();
     };
 
     issue(st0, 0);
-    issue(st1, 1);
-    issue(st2, 2);
-    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     read_frags(st0, 0, fa, fb);
-    for (int kt = 0; kt < nk; kt += kStages) {
-        iteration(st0, st1, st3, kt);
-        iteration(st1, st2, st0, kt + 1);
-        iteration(st2, st3, st1, kt + 2);
-        iteration(st3, st0, st2, kt + 3);
+    for (int kt = 0; kt < nk; kt += 2) {
+        iteration(st0, st1, kt);
+        iteration(st1, st0, kt + 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogues. Lane l, block (i, j), register group rg holds rows
     // lr0..lr0+3 of column lc (tile-local).
     if (STAGE == 0 || STAGE == 1) {
-        const int64_t ld = M.mp;
+        const int64_t ld = M.ldt;
         OpT* out = static_cast<OpT*>(STAGE == 0 ? M.a : M.b);
         const OpT* ain = static_cast<const OpT*>(M.a);
         const bool diag = t.bi == t.bj;
@@ -636,10 +694,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         }
     } else {
         const int nxt = cur ^ 1;
-        const int64_t ldx = M.np, ldt = M.mp;
+        const int64_t ldx = M.ldx, ldt = M.ldt, ldf = M.ldf;
         // fp32 X before the step, stored like X^T: the bf16 path's master, or
         // the fp32 path's operand copy (read-only in this launch).
         const float* src = M.xft ? M.xft : static_cast<const float*>(M.xt[cur]);
+        const int64_t lds = M.xft ? ldf : ldt;
         float* xft = M.xft;
         OpT* xb = static_cast<OpT*>(M.xb[nxt]);
         OpT* xt = static_cast<OpT*>(M.xt[nxt]);
@@ -655,7 +714,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                 for (int rg = 0; rg < 4; ++rg) {
                     const int64_t r0 = gbi + wr * 128 + i * 32 + rg * 8 + fg * 4;
                     const int64_t c = gbj + wc * 128 + j * 32 + fr;
-                    xv[j][rg] = load4(src + c * ldt + r0);
+                    xv[j][rg] = load4(src + c * lds + r0);
                 }
             auto group = [&](int64_t r0, int64_t c, const f32x4& x, float v0, float v1, float v2,
                              float v3) {
@@ -663,10 +722,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                               fmaf(ca, x[3], v3)};
                 if (!last) {
                     if (xft)
-                        store4(xft + c * ldt + r0, y[0], y[1], y[2], y[3]);
+                        store4(xft + c * ldf + r0, y[0], y[1], y[2], y[3]);
+                    if (!IsBf16<OpT>::value) {   // the bf16 path keeps no row-major X
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
+                        for (int e = 0; e < 4; ++e)
+                            xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
+                    }
                     store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
                 } else if (c < M.n) {
 #pragma unroll

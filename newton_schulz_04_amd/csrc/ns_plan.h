@@ -21,6 +21,7 @@ struct PlanMat {
     int32_t index;          // position in the caller's batch
     int64_t rows, cols;
     int32_t m, n, mp, np, trans;
+    int32_t ldx, ldt, ldf;  // row pitches in elements (see row_pitch)
     int64_t cost;
     MatClass cls;
 };
