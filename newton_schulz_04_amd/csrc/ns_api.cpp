@@ -209,20 +209,21 @@ void build_meta(const Plan& p, void* const* ptrs, char* ws, char* meta, std::vec
         d.np = pm.np;
         d.ldx = pm.ldx;
         d.ldt = pm.ldt;
-        d.ldf = pm.ldf;
         d.trans = pm.trans;
         d.batch_index = pm.index;
         d.part_begin = p.part_prefix[li];
         d.nparts = p.part_prefix[li + 1] - p.part_prefix[li];
         d.prep_begin = p.prep_prefix[li];
         d.nprep = p.prep_prefix[li + 1] - p.prep_prefix[li];
-        d.xft = static_cast<float*>(ws_at(lo.xf));
+        d.xlo = ws_at(lo.xlo);
         for (int s = 0; s < 2; ++s) {
             d.xb[s] = ws_at(lo.xb[s]);
             d.xt[s] = ws_at(lo.xt[s]);
         }
         d.a = ws_at(lo.a);
         d.b = ws_at(lo.b);
+        d.adiag = static_cast<float*>(ws_at(lo.adiag));
+        d.bdiag = static_cast<float*>(ws_at(lo.bdiag));
         std::memcpy(h + p.meta_large + li * sizeof(ns::LargeMat), &d, sizeof d);
     }
     for (size_t si = 0; si < p.small.size(); ++si) {

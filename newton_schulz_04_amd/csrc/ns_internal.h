@@ -38,16 +38,18 @@ struct LargeMat {
     int32_t mp, np;    // padded dims
     int32_t ldx;       // row pitch (elements) of xb: rows of np
     int32_t ldt;       // row pitch (elements) of xt, a, b: rows of mp
-    int32_t ldf;       // row pitch (elements) of xft: rows of mp fp32
     int32_t trans;     // 1 when rows > cols (X = G^T)
     int32_t batch_index;
     int32_t part_begin, nparts;   // norm partial sums [part_begin, +nparts)
     int32_t prep_begin, nprep;    // normalize tiles   [prep_begin, +nprep)
-    float* xft;        // fp32 master of X stored transposed, np x mp (bf16 path only)
+    void* xlo;         // bf16 path: X - bf16(X), bf16, stored like X^T (np x ldt);
+                       // with xt it carries X to about 17 significant bits
     void* xb[2];       // X operand copies, mp x np, ping-pong
     void* xt[2];       // X^T operand copies, np x mp, ping-pong
     void* a;           // A = X X^T, mp x mp
     void* b;           // B = bA + cA^2, mp x mp
+    float* adiag;      // bf16 path: A_ii - bf16(A_ii), mp floats
+    float* bdiag;      // bf16 path: B_ii - bf16(B_ii), mp floats
 };
 
 // One matrix of the fused small path.

@@ -10,8 +10,9 @@
 //   k_norm_partial sum of squares of a 16K-element piece of G (wave shuffles).
 //   k_norm_final   folds the pieces of a matrix in fixed order -> 1/(||G||+eps).
 //   k_prep         X = G/(||G||+eps), transposed when rows > cols, zero-padded
-//                  to multiples of 256; writes the X / X^T operand copies and
-//                  the fp32 master (stored like X^T) through a 64x64 LDS tile.
+//                  to multiples of 256; writes X^T (bf16: X_hi = bf16(X) and
+//                  X_lo = bf16(X - X_hi); fp32: X^T and X) through a 64x64 LDS
+//                  tile.
 //   k_gemm<stage>  grouped 256x256 MFMA GEMM over a tile list, C = P Q^T with
 //                  both operands K-contiguous in memory:
 //                    stage 0  P = Q = X            -> A (upper tiles, mirrored)
@@ -323,9 +324,10 @@ __device__ __forceinline__ void put_x(const LargeMat& M, int64_t i, int64_t j, f
 template <typename T>
 __device__ __forceinline__ void put_xt(const LargeMat& M, int64_t i, int64_t j, float v)
 {
-    if (M.xft)
-        M.xft[j * M.ldf + i] = v;
-    static_cast<T*>(M.xt[0])[j * M.ldt + i] = from_f32<T>(v);
+    const T hi = from_f32<T>(v);
+    static_cast<T*>(M.xt[0])[j * M.ldt + i] = hi;
+    if (M.xlo)   // bf16 path: the part of X that bf16 drops
+        static_cast<T*>(M.xlo)[j * M.ldt + i] = from_f32<T>(v - to_f32(hi));
 }
 
 template <typename T>
@@ -408,6 +410,8 @@ constexpr int kStageRowBytes = 128;
 constexpr int kStageOpBytes = kTile * kStageRowBytes;   // 32 KB
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int H> struct Peel { static constexpr int value = H; };
 
 template <typename OpT> struct Mfma;
 template <> struct Mfma<bf16> {
@@ -521,8 +525,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     const int dma_voff = kTrans ? dma_row * ldb + (((lane & 31) ^ tr_swz(dma_row)) << 4)
                                 : dma_row * ldb + (((lane & 7) ^ lds_swz(dma_row)) << 4);
 
-    auto issue = [&](char* sp, int kt) {
-        kt = kt < nk ? kt : nk - 1;   // past the end: reload the last k-tile
+    // The bf16 update visits the k-tiles starting at this tile's own 256 rows
+    // (k-tile kb), wrapping around; the order is fixed per tile. Loop position
+    // kk = nk (past the end) reloads k-tile kb, which is never read.
+    constexpr bool kIdent = STAGE == 2 && IsBf16<OpT>::value;
+    const int kb = kIdent ? t.bi * 4 : 0;
+    auto issue = [&](char* sp, int kk) {
+        const int kt = kk + kb >= nk ? kk + kb - nk : kk + kb;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int soff = kTrans ? (kt * 64 + 8 * q) * ldb : kt * kStageRowBytes + q * 32 * ldb;
@@ -608,30 +617,90 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // waits for its own DMA and passes the barrier (so `oth` is complete and
     // nobody reads `cur` any more), reads k-step 0 of `oth` and issues the
     // last k-step's MFMAs to cover that read.
+    // bf16 X <- aX + BX: the a X_hi part (X_hi = bf16(X), the Q operand
+    // itself) is added by the MFMAs too. Wavefront row wr holds rows
+    // 128 wr .. 128 wr + 127 of the tile, which are k-tiles 2 wr and 2 wr + 1
+    // of the first four the loop visits; there, an identity A fragment
+    // scaled by s_hi = bf16(s) and one scaled by s_lo = bf16(s - s_hi)
+    // multiply the Q fragments already in registers (k-step ks of k-tile h
+    // covers rows 16 (ks & 1) .. + 15 of 32-row block 2 (h & 1) + ks / 2).
+    // The other wavefront row adds zeros there, so the code stays straight.
+    // Those products are exact in fp32; a X_lo is added in the epilogue.
+    // (The scale a is per row: see rowscale.)
+    // Per-row scale of the identity: a + (B_ii - bf16(B_ii)), which also
+    // restores the part of B's diagonal that its bf16 operand dropped (the
+    // diagonal dominates B when the singular values are clustered).
+    float rowscale[4];
+    if constexpr (kIdent) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            rowscale[ii] = ca + M.bdiag[gbi + wr * 128 + ii * 32 + fr];
+    }
+    auto ident = [&](int h, int ks, const uint4 (&bfr)[4]) {
+        const int ii = 2 * (h & 1) + (ks >> 1);
+        // A fragment: lane l holds row l & 31, k = 8 (l >> 5) + e of the
+        // 32 x 16 block; the identity sits at e = (l & 31) - 16 (ks & 1) - 8 (l >> 5).
+        const int e = fr - 16 * (ks & 1) - 8 * fg;
+        const bool mine = (h >> 1) == wr;
+        const bf16 ahi = (bf16)rowscale[ii];
+        const bf16 alo = (bf16)(rowscale[ii] - (float)ahi);
+        const uint32_t hb = mine ? __builtin_bit_cast(uint16_t, ahi) : 0u;
+        const uint32_t lb = mine ? __builtin_bit_cast(uint16_t, alo) : 0u;
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const bool on = (e >> 1) == w && e >= 0 && e < 8;
+            const int sh = (e & 1) * 16;
+            wh[w] = on ? hb << sh : 0u;
+            wl[w] = on ? lb << sh : 0u;
+        }
+        const uint4 fh = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        const uint4 fl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            Mfma<OpT>::mac(acc[ii][j], fh, bfr[j]);
+            Mfma<OpT>::mac(acc[ii][j], fl, bfr[j]);
+        }
+    };
+
     uint4 fa[4], fb[4], ga[4], gb[4];
-    auto iteration = [&](const char* cur, char* oth, int kt) {
-        issue(oth, kt + 1);
+    // H >= 0: one of the first four k-tiles of the bf16 update (adds a X_hi)
+    auto iteration = [&](const char* cur, char* oth, int kk, auto peel) {
+        constexpr int H = decltype(peel)::value;
+        issue(oth, kk + 1);
         read_frags(cur, 1, ga, gb);
         mfma_block(fa, fb);
         interleave();
+        if constexpr (H >= 0) ident(H, 0, fb);
         read_frags(cur, 2, fa, fb);
         mfma_block(ga, gb);
         interleave();
+        if constexpr (H >= 0) ident(H, 1, gb);
         read_frags(cur, 3, ga, gb);
         mfma_block(fa, fb);
         interleave();
+        if constexpr (H >= 0) ident(H, 2, fb);
         asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         read_frags(oth, 0, fa, fb);
         mfma_block(ga, gb);
         interleave();
+        if constexpr (H >= 0) ident(H, 3, gb);
     };
 
     issue(st0, 0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     read_frags(st0, 0, fa, fb);
-    for (int kt = 0; kt < nk; kt += 2) {
-        iteration(st0, st1, kt);
-        iteration(st1, st0, kt + 1);
+    int kk = 0;
+    if constexpr (kIdent) {
+        iteration(st0, st1, 0, Peel<0>{});
+        iteration(st1, st0, 1, Peel<1>{});
+        iteration(st0, st1, 2, Peel<2>{});
+        iteration(st1, st0, 3, Peel<3>{});
+        kk = 4;
+    }
+    for (; kk < nk; kk += 2) {
+        iteration(st0, st1, kk, Peel<-1>{});
+        iteration(st1, st0, kk + 1, Peel<-1>{});
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -642,12 +711,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         OpT* out = static_cast<OpT*>(STAGE == 0 ? M.a : M.b);
         const OpT* ain = static_cast<const OpT*>(M.a);
         const bool diag = t.bi == t.bj;
+        // bf16: the diagonals of A and B also keep what their bf16 rounding
+        // drops (d_i = v_ii - bf16(v_ii)). With A = A_bf16 + diag(dA), the
+        // first-order B is bA_bf16 + c A_bf16^2 + b diag(dA)
+        // + c A_bf16,ij (dA_i + dA_j); the update adds B's own residue.
+        constexpr bool kDiag = IsBf16<OpT>::value;
+        float* dout = STAGE == 0 ? M.adiag : M.bdiag;
+        float dcol[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kDiag && STAGE == 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dcol[j] = M.adiag[gbj + wc * 128 + j * 32 + fr];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             // bA + cA^2 needs A at the same places; A is exactly symmetric, so
             // rows r0..r0+3 of column c are A[c][r0..r0+3], one vector load.
             // All 16 loads of a block row are issued before any is used.
             f32x4 a4[4][4];
+            f32x4 drow[4];
+            if constexpr (kDiag && STAGE == 1) {
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg)
+                    drow[rg] = *reinterpret_cast<const f32x4*>(M.adiag + gbi + wr * 128 + i * 32 + rg * 8 +
+                                                              fg * 4);
+            }
             if (STAGE == 1) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -671,8 +759,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                         v[e] = acc[i][j][rg * 4 + e];
                     if (STAGE == 1) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            v[e] = cb * a4[j][rg][e] + cc * v[e];
+                        for (int e = 0; e < 4; ++e) {
+                            float ce = cb;
+                            if constexpr (kDiag)
+                                ce = fmaf(cc, drow[rg][e] + dcol[j], cb);
+                            v[e] = ce * a4[j][rg][e] + cc * v[e];
+                        }
                     }
                     if (!diag) {
 #pragma unroll
@@ -684,29 +776,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                         // so the stored matrix is exactly symmetric.
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            if (lr0 + e <= lc)
+                            if (lr0 + e < lc) {
                                 out[(r0 + e) * ld + c] = from_f32<OpT>(v[e]);
-                            if (lr0 + e < lc)
                                 out[c * ld + r0 + e] = from_f32<OpT>(v[e]);
+                            }
                         }
                     }
                 }
         }
+        if (diag && wr == wc) {
+            // The diagonal: in block (i, i), lane (fr, fg) holds element
+            // (fr, fr) when fg == (fr >> 2) & 1, in register 4 (fr >> 3) + (fr & 3).
+            const int sel = 4 * (fr >> 3) + (fr & 3);
+            const bool has = fg == ((fr >> 2) & 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    v = r == sel ? acc[i][i][r] : v;
+                const int64_t rc = gbi + wr * 128 + i * 32 + fr;
+                if (has) {
+                    if (STAGE == 1) {
+                        const float av = to_f32(ain[rc * ld + rc]);
+                        float ce = cb;
+                        if constexpr (kDiag) {
+                            const float da = M.adiag[rc];
+                            ce = fmaf(cc, 2.f * da, cb);
+                            v = fmaf(cb, da, ce * av + cc * v);
+                        } else {
+                            v = ce * av + cc * v;
+                        }
+                    }
+                    const OpT vb = from_f32<OpT>(v);
+                    out[rc * ld + rc] = vb;
+                    if constexpr (kDiag)
+                        dout[rc] = v - to_f32(vb);
+                }
+            }
+        }
     } else {
         const int nxt = cur ^ 1;
-        const int64_t ldx = M.ldx, ldt = M.ldt, ldf = M.ldf;
-        // fp32 X before the step, stored like X^T: the bf16 path's master, or
-        // the fp32 path's operand copy (read-only in this launch).
-        const float* src = M.xft ? M.xft : static_cast<const float*>(M.xt[cur]);
-        const int64_t lds = M.xft ? ldf : ldt;
-        float* xft = M.xft;
+        const int64_t ldx = M.ldx, ldt = M.ldt;
+        // The part of aX not yet in the accumulators, per lane four rows of a
+        // column, stored like X^T: a X_lo on the bf16 path (X_hi was added by
+        // the identity MFMAs), a X on the fp32 path (its operand copy,
+        // read-only in this launch).
+        const OpT* src = static_cast<const OpT*>(kIdent ? M.xlo : M.xt[cur]);
+        OpT* xlo = static_cast<OpT*>(M.xlo);
         OpT* xb = static_cast<OpT*>(M.xb[nxt]);
         OpT* xt = static_cast<OpT*>(M.xt[nxt]);
         OpT* user = static_cast<OpT*>(M.user);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // All 16 loads of a block row first (a lane's four rows of a
-            // column are one 16-byte load), then y = aX + BX and the stores.
+            // All 16 loads of a block row first, then the sums and stores.
             f32x4 xv[4][4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -714,21 +837,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                 for (int rg = 0; rg < 4; ++rg) {
                     const int64_t r0 = gbi + wr * 128 + i * 32 + rg * 8 + fg * 4;
                     const int64_t c = gbj + wc * 128 + j * 32 + fr;
-                    xv[j][rg] = load4(src + c * lds + r0);
+                    xv[j][rg] = load4(src + c * ldt + r0);
                 }
             auto group = [&](int64_t r0, int64_t c, const f32x4& x, float v0, float v1, float v2,
                              float v3) {
                 float y[4] = {fmaf(ca, x[0], v0), fmaf(ca, x[1], v1), fmaf(ca, x[2], v2),
                               fmaf(ca, x[3], v3)};
                 if (!last) {
-                    if (xft)
-                        store4(xft + c * ldf + r0, y[0], y[1], y[2], y[3]);
-                    if (!IsBf16<OpT>::value) {   // the bf16 path keeps no row-major X
+                    store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
+                    if (kIdent) {
+                        // new X = X_hi (just stored) + X_lo
+                        float lo[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            lo[e] = y[e] - to_f32(from_f32<OpT>(y[e]));
+                        store4(xlo + c * ldt + r0, lo[0], lo[1], lo[2], lo[3]);
+                    } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
                     }
-                    store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
                 } else if (c < M.n) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {

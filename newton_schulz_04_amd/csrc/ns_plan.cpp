@@ -163,7 +163,6 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
             pm.np = pad_to(pm.n, kTile);
             pm.ldx = row_pitch(pm.np, p.elt);
             pm.ldt = row_pitch(pm.mp, p.elt);
-            pm.ldf = row_pitch(pm.mp, 4);
             // Tile coordinates are int16 and a 256-row operand block must fit
             // a 32-bit buffer range.
             if (pm.np / kTile > 32767 || (int64_t)pm.np * (int64_t)p.elt * kTile >= (int64_t(1) << 31) ||
@@ -214,10 +213,10 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
         const size_t sq_bytes = p.elt * (size_t)pm.mp * pm.ldt;   // mp rows of mp
         LargeOffsets lo{};
         if (dtype == 0) {
-            lo.xf = off;
-            off = align_up(off + 4 * (size_t)pm.np * pm.ldf);
+            lo.xlo = off;
+            off = align_up(off + xt_bytes);
         } else {
-            lo.xf = SIZE_MAX;
+            lo.xlo = SIZE_MAX;
         }
         for (int s = 0; s < 2; ++s) {
             if (dtype == 0) {
@@ -233,6 +232,14 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
         off = align_up(off + sq_bytes);
         lo.b = off;
         off = align_up(off + sq_bytes);
+        if (dtype == 0) {
+            lo.adiag = off;
+            off = align_up(off + 4 * (size_t)pm.mp);
+            lo.bdiag = off;
+            off = align_up(off + 4 * (size_t)pm.mp);
+        } else {
+            lo.adiag = lo.bdiag = SIZE_MAX;
+        }
         p.large_off.push_back(lo);
     }
     for (int32_t idx : p.small) {

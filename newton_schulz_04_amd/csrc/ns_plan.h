@@ -21,14 +21,14 @@ struct PlanMat {
     int32_t index;          // position in the caller's batch
     int64_t rows, cols;
     int32_t m, n, mp, np, trans;
-    int32_t ldx, ldt, ldf;  // row pitches in elements (see row_pitch)
+    int32_t ldx, ldt;  // row pitches in elements (see row_pitch)
     int64_t cost;
     MatClass cls;
 };
 
 // Byte offsets into the workspace; the planner lays everything out from 0.
 struct LargeOffsets {
-    size_t xf, xb[2], xt[2], a, b;
+    size_t xlo, xb[2], xt[2], a, b, adiag, bdiag;
 };
 
 struct Plan {

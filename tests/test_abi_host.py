@@ -183,7 +183,7 @@ def test_workspace_bytes():
     b = ns.workspace_bytes([(8192, 6144)], ns.NS_BF16)
     mp, np_ = 6144, 8192
     ldt = mp + 64          # 12 KB bf16 rows are padded by 128 bytes
-    # fp32 master (X^T layout), two bf16 X^T copies, A and B; no row-major X
-    data = 4 * mp * np_ + 2 * 2 * np_ * ldt + 2 * 2 * mp * ldt
+    # X_lo and two X_hi copies (X^T layout, bf16), A and B; no row-major X
+    data = 2 * np_ * ldt + 2 * 2 * np_ * ldt + 2 * 2 * mp * ldt
     assert data <= b <= data + (1 << 20)
     assert ns.workspace_bytes([(0, 3)], ns.NS_BF16) <= 4096   # metadata only

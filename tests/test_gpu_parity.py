@@ -45,12 +45,29 @@ def test_attn_gate_workload_padded():
 
 
 LARGE_SHAPES = [(300, 520), (520, 300), (256, 256), (33, 100), (100, 33), (257, 513),
-                (513, 257), (64, 2000), (700, 1000), (1000, 700), (96, 96)]
+                (513, 257), (64, 2000), (700, 1000), (1000, 700), (96, 96),
+                # few rows, many columns: clustered singular values, where the
+                # diagonals of A and B dominate and their rounding matters most
+                (33, 1000), (1000, 33), (64, 2304)]
 
 
 @pytest.mark.parametrize("shape", LARGE_SHAPES)
 def test_large_bf16_vs_oracle(shape):
     g = workloads.gaussian(shape, seed=11, index=shape[0] * 7 + shape[1])
+    (y,) = gpu_run([g])
+    e = rel_err(y, oracle_run(g))
+    assert e <= TOL[torch.bfloat16], e
+
+
+@pytest.mark.parametrize("rank,shape", [(16, (256, 1024)), (40, (600, 300)), (1, (96, 700))])
+def test_low_rank_bf16_vs_oracle(rank, shape):
+    # Exactly low-rank input: directions outside the row space grow by about
+    # a per step from whatever rounding puts there, so X must be carried
+    # between steps more precisely than one bf16 rounding.
+    gen = torch.Generator().manual_seed(rank * 1000 + shape[0])
+    left = torch.randn((shape[0], rank), generator=gen, dtype=torch.float64)
+    right = torch.randn((rank, shape[1]), generator=gen, dtype=torch.float64)
+    g = (left @ right).to(torch.bfloat16)
     (y,) = gpu_run([g])
     e = rel_err(y, oracle_run(g))
     assert e <= TOL[torch.bfloat16], e
