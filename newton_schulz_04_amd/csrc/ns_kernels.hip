@@ -458,6 +458,141 @@ __device__ __forceinline__ uint2 ds_read_tr(const char* p)
         (__attribute__((address_space(3))) v4i16*)(p)));
 }
 
+// Epilogue of the bf16 update, staged through the 128 KB of LDS that the K
+// loop no longer needs, so that global memory sees whole 512-byte column
+// segments of the X^T layout instead of 16-byte pieces of 32 columns.
+//
+// LDS layout: tile column c (0..255) is a 512-byte row at (c & 127) * 512 of
+// st0 (c < 128) or st1; its 16-byte chunk q (rows 8q..8q+7) sits at chunk
+// q ^ (c & 31), so the accumulator-order accesses (32 columns x one chunk)
+// spread over the banks. Every element is read and rewritten by the same
+// lane in the accumulator phase, so only the copy phases need barriers.
+//
+//   X_lo tile -> LDS (DMA), y = acc + a X_lo, LDS <- bf16(y), acc <- y - bf16(y)
+//   LDS -> X_hi (next slot), LDS <- bf16(acc), LDS -> X_lo (in place)
+// On the last step bf16(y) goes to the caller's buffer instead.
+__device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st0, char* st1,
+                                                     f32x16 (&acc)[4][4], int64_t gbi, int64_t gbj,
+                                                     int nxt, int last, float ca, int wave,
+                                                     int lane)
+{
+    const int64_t ldt = M.ldt;
+    const int fr = lane & 31, fg = lane >> 5;
+    const int wr = wave >> 1, wc = wave & 1;
+    // Copy phases: wavefront w moves tile columns 64w .. 64w + 63, two per
+    // instruction (lanes 0-31 and 32-63), lane p = l & 31 taking stored chunk p.
+    char* stw = wave < 2 ? st0 : st1;
+    const int half = lane >> 5, p = lane & 31;
+    // Accumulator phases: this lane's columns wc*128 + 32 j + fr live in one buffer.
+    char* stm = wc ? st1 : st0;
+
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+        const bf16* lo_g = static_cast<const bf16*>(M.xlo) + gbj * ldt + gbi;
+        const __amdgpu_buffer_rsrc_t rlo = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)lo_g, (short)0, (int)(kTile * ldt * 2), 0x00020000);
+#pragma unroll 4
+        for (int q = 0; q < 32; ++q) {
+            const int tc = wave * 64 + 2 * q + half;
+            const int voff = (int)(tc * ldt * 2) + ((p ^ (tc & 31)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rlo, (lds_ptr_t)(stw + ((wave & 1) * 64 + 2 * q) * 512), 16, voff, 0, 0, 0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+    const bool staged = !last || M.trans;
+    bf16* user = static_cast<bf16*>(M.user);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int q = wr * 16 + i * 4 + rg;
+                char* a = stm + (j * 32 + fr) * 512 + ((q ^ fr) << 4) + (fg << 3);
+                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(a);
+                float y[4];
+                bf16x4 hi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[e] = fmaf(ca, (float)lo[e], acc[i][j][rg * 4 + e]);
+                    hi[e] = (bf16)y[e];
+                    acc[i][j][rg * 4 + e] = y[e] - (float)hi[e];
+                }
+                if (staged) {
+                    *reinterpret_cast<bf16x4*>(a) = hi;
+                } else {
+                    // last step, caller's buffer row-major in the oriented layout
+                    const int64_t r0 = gbi + q * 8 + fg * 4;
+                    const int64_t c = gbj + wc * 128 + j * 32 + fr;
+                    if (c < M.n) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (r0 + e < M.m)
+                                user[(r0 + e) * M.cols + c] = hi[e];
+                    }
+                }
+            }
+    if (!staged)
+        return;
+
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (!last) {
+        bf16* xt = static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi;
+#pragma unroll 4
+        for (int q = 0; q < 32; ++q) {
+            const int tc = wave * 64 + 2 * q + half;
+            const uint4 v = *reinterpret_cast<const uint4*>(stw + ((wave & 1) * 64 + 2 * q + half) * 512 + p * 16);
+            *reinterpret_cast<uint4*>(xt + tc * ldt + 8 * (p ^ (tc & 31))) = v;
+        }
+    } else {
+        // last step, rows > cols: the caller's buffer is X^T, rows of M.cols
+#pragma unroll 4
+        for (int q = 0; q < 32; ++q) {
+            const int tc = wave * 64 + 2 * q + half;
+            const int64_t c = gbj + tc, r0 = gbi + 8 * (p ^ (tc & 31));
+            const uint4 v = *reinterpret_cast<const uint4*>(stw + ((wave & 1) * 64 + 2 * q + half) * 512 + p * 16);
+            if (c < M.n) {
+                bf16* dst = user + c * M.cols + r0;
+                if (r0 + 8 <= M.m && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                    *reinterpret_cast<uint4*>(dst) = v;
+                } else {
+                    const bf16x8 h = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (r0 + e < M.m)
+                            dst[e] = h[e];
+                }
+            }
+        }
+        return;
+    }
+
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int q = wr * 16 + i * 4 + rg;
+                bf16x4 lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    lo[e] = (bf16)acc[i][j][rg * 4 + e];
+                *reinterpret_cast<bf16x4*>(stm + (j * 32 + fr) * 512 + ((q ^ fr) << 4) + (fg << 3)) = lo;
+            }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    bf16* xlo = static_cast<bf16*>(M.xlo) + gbj * ldt + gbi;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+        const int tc = wave * 64 + 2 * q + half;
+        const uint4 v = *reinterpret_cast<const uint4*>(stw + ((wave & 1) * 64 + 2 * q + half) * 512 + p * 16);
+        *reinterpret_cast<uint4*>(xlo + tc * ldt + 8 * (p ^ (tc & 31))) = v;
+    }
+}
+
 template <typename OpT, int STAGE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
                                                       const Tile* __restrict__ tiles, int cur,
@@ -818,6 +953,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     } else {
         const int nxt = cur ^ 1;
         const int64_t ldx = M.ldx, ldt = M.ldt;
+        if constexpr (kIdent) {
+            update_epilogue_bf16(M, st0, st1, acc, gbi, gbj, nxt, last, ca, wave, lane);
+            return;
+        }
         // The part of aX not yet in the accumulators, per lane four rows of a
         // column, stored like X^T: a X_lo on the bf16 path (X_hi was added by
         // the identity MFMAs), a X on the fp32 path (its operand copy,
