@@ -89,6 +89,23 @@ def metric_flops_per_kind(shapes):
     return f
 
 
+def measured_traffic(workload, kind):
+    """HBM bytes per launch of `kind` from the committed PMC summary of this
+    workload, or None when there is none or the library sources changed since
+    the counters were taken."""
+    from newton_schulz_04_amd.profiling import source_hash
+    path = os.path.join(ROOT, "profiles", f"k_gemm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_hash():
+        log("traffic: PMC summary predates the current sources; reporting null")
+        return None
+    entry = rec.get("kernels", {}).get(kind)
+    return entry.get("bytes") if entry else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dense_lowrank")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB device copy first (calibrates PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -107,6 +126,14 @@ def main():
     from newton_schulz_04_amd import workloads as wl
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        from newton_schulz_04_amd.profiling import COPY_PROBE_BYTES
+        src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: {COPY_PROBE_BYTES} bytes device to device")
     log(f"library {ns.version()}; generating workload {args.workload}")
     mats, desc = make_workload(args.workload)
     shapes = [tuple(m.shape) for m in mats]
@@ -172,7 +199,8 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload, dom)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -37,6 +37,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Element type of a dtype code (0 = bf16, 1 = fp32). Kernels are templated on
+// the code rather than the type so that their names demangle in profilers.
+template <int DT> struct Elt;
+template <> struct Elt<0> { using type = bf16; };
+template <> struct Elt<1> { using type = float; };
+
 constexpr float kEps = 1e-7f;
 constexpr int kThreads = 256;
 
@@ -109,10 +115,11 @@ __device__ __forceinline__ int find_mat(const int32_t* prefix, int nmats, int b)
 //               partial A's are added in wavefront order.
 //   B = bA + cA^2 in LDS.
 //   X <- aX + BX column by column; thread t owns columns t, t+256, ...
-template <typename T>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__ mats,
                                                     int steps, float ca, float cb, float cc)
 {
+    using T = typename Elt<DT>::type;
     __shared__ float red[4];
     __shared__ float xs[64][33];
     __shared__ float part[4][32][33];
@@ -233,12 +240,13 @@ __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__
 // Norm, pass 1: one workgroup per kNormChunk elements of G (row-major). Thread
 // t accumulates elements (t + 256 q) * V + e, q outer, e inner, V = 16 bytes
 // of elements; lanes fold by butterfly, wavefronts in order.
-template <typename T>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void k_norm_partial(const LargeMat* __restrict__ mats,
                                                            int nmats,
                                                            const int32_t* __restrict__ prefix,
                                                            float* __restrict__ partials)
 {
+    using T = typename Elt<DT>::type;
     __shared__ float red[4];
     constexpr int V = 16 / sizeof(T);
     constexpr int Q = kNormChunk / (kThreads * V);
@@ -295,12 +303,13 @@ __global__ __launch_bounds__(kThreads) void k_norm_final(const int32_t* __restri
 }
 
 // steps == 0: G <- G * inv, same pieces as the norm.
-template <typename T>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void k_scale_out(const LargeMat* __restrict__ mats,
                                                         int nmats,
                                                         const int32_t* __restrict__ prefix,
                                                         const float* __restrict__ inv)
 {
+    using T = typename Elt<DT>::type;
     const int b = blockIdx.x;
     const int mi = find_mat(prefix, nmats, b);
     const LargeMat& M = mats[mi];
@@ -330,11 +339,12 @@ __device__ __forceinline__ void put_xt(const LargeMat& M, int64_t i, int64_t j, 
         static_cast<T*>(M.xlo)[j * M.ldt + i] = from_f32<T>(v - to_f32(hi));
 }
 
-template <typename T>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ mats, int nmats,
                                                    const int32_t* __restrict__ prefix,
                                                    const float* __restrict__ inv)
 {
+    using T = typename Elt<DT>::type;
     __shared__ float tile[kPrepTile][kPrepTile + 1];
     const int b = blockIdx.x;
     const int mi = find_mat(prefix, nmats, b);
@@ -458,19 +468,66 @@ __device__ __forceinline__ uint2 ds_read_tr(const char* p)
         (__attribute__((address_space(3))) v4i16*)(p)));
 }
 
-// Epilogue of the bf16 update, staged through the 128 KB of LDS that the K
-// loop no longer needs, so that global memory sees whole 512-byte column
-// segments of the X^T layout instead of 16-byte pieces of 32 columns.
-//
-// LDS layout: tile column c (0..255) is a 512-byte row at (c & 127) * 512 of
-// st0 (c < 128) or st1; its 16-byte chunk q (rows 8q..8q+7) sits at chunk
-// q ^ (c & 31), so the accumulator-order accesses (32 columns x one chunk)
-// spread over the banks. Every element is read and rewritten by the same
-// lane in the accumulator phase, so only the copy phases need barriers.
-//
-//   X_lo tile -> LDS (DMA), y = acc + a X_lo, LDS <- bf16(y), acc <- y - bf16(y)
+// After the K loop the two LDS stages (128 KB) hold one 256 x 256 bf16 tile
+// for the epilogues: row R (0..255) is 512 bytes at (R & 127) * 512 of st0
+// (R < 128) or st1, and its 16-byte chunk q (elements 8q .. 8q + 7) is stored
+// at chunk q ^ (R & 31). Accesses of 32 rows x one chunk (the accumulator
+// order) and of whole rows then spread over the LDS banks, and global memory
+// sees whole 512-byte rows instead of 16-byte pieces of 32 rows.
+struct LdsTile {
+    char* st0;
+    char* st1;
+    __device__ __forceinline__ char* row(int R) const { return (R < 128 ? st0 : st1) + (R & 127) * 512; }
+    // element x (0..255) of row R
+    __device__ __forceinline__ char* at(int R, int x) const
+    {
+        return row(R) + (((x >> 3) ^ (R & 31)) << 4) + (x & 7) * 2;
+    }
+};
+
+// Whole-tile moves between an LdsTile and global rows of 256 bf16 at a pitch
+// of ld elements. Wavefront w moves rows 64w .. 64w + 63, two per instruction
+// (lanes 0-31 and 32-63), lane p = l & 31 taking stored chunk p.
+__device__ __forceinline__ void tile_load(const LdsTile& T, const bf16* src, int64_t ld, int wave,
+                                          int lane)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)src, (short)0, (int)(kTile * ld * 2), 0x00020000);
+    const int half = lane >> 5, p = lane & 31;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+        const int R = wave * 64 + 2 * q + half;
+        const int voff = (int)(R * ld * 2) + ((p ^ (R & 31)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)T.row(wave * 64 + 2 * q), 16, voff, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void tile_store(const LdsTile& T, bf16* dst, int64_t ld, int wave, int lane)
+{
+    const int half = lane >> 5, p = lane & 31;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+        const int R = wave * 64 + 2 * q + half;
+        const uint4 v = *reinterpret_cast<const uint4*>(T.row(R) + p * 16);
+        *reinterpret_cast<uint4*>(dst + R * ld + 8 * (p ^ (R & 31))) = v;
+    }
+}
+
+#define NS_WAIT_ALL_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+#define NS_WAIT_DMA_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory")
+#define NS_WAIT_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+// In the epilogues, lane (fr, fg) of wavefront (wr, wc) holds, in block
+// (i, j) register 4 rg + e, tile element (r, c) with
+// r = 128 wr + 32 i + 8 rg + 4 fg + e and c = 128 wc + 32 j + fr: four
+// consecutive r of one c, i.e. 8 bytes of LdsTile row c.
+
+// Epilogue of the bf16 update (X^T layout, LdsTile row = tile column c):
+//   X_lo tile -> LDS, y = acc + a X_lo, LDS <- bf16(y), acc <- y - bf16(y)
 //   LDS -> X_hi (next slot), LDS <- bf16(acc), LDS -> X_lo (in place)
-// On the last step bf16(y) goes to the caller's buffer instead.
+// Every element is read and rewritten by the same lane in the accumulator
+// passes, so only the copies need barriers. On the last step bf16(y) goes to
+// the caller's buffer instead.
 __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st0, char* st1,
                                                      f32x16 (&acc)[4][4], int64_t gbi, int64_t gbj,
                                                      int nxt, int last, float ca, int wave,
@@ -479,27 +536,12 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st
     const int64_t ldt = M.ldt;
     const int fr = lane & 31, fg = lane >> 5;
     const int wr = wave >> 1, wc = wave & 1;
-    // Copy phases: wavefront w moves tile columns 64w .. 64w + 63, two per
-    // instruction (lanes 0-31 and 32-63), lane p = l & 31 taking stored chunk p.
-    char* stw = wave < 2 ? st0 : st1;
-    const int half = lane >> 5, p = lane & 31;
-    // Accumulator phases: this lane's columns wc*128 + 32 j + fr live in one buffer.
-    char* stm = wc ? st1 : st0;
+    const LdsTile T{st0, st1};
+    bf16* lo_g = static_cast<bf16*>(M.xlo) + gbj * ldt + gbi;
 
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    {
-        const bf16* lo_g = static_cast<const bf16*>(M.xlo) + gbj * ldt + gbi;
-        const __amdgpu_buffer_rsrc_t rlo = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)lo_g, (short)0, (int)(kTile * ldt * 2), 0x00020000);
-#pragma unroll 4
-        for (int q = 0; q < 32; ++q) {
-            const int tc = wave * 64 + 2 * q + half;
-            const int voff = (int)(tc * ldt * 2) + ((p ^ (tc & 31)) << 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rlo, (lds_ptr_t)(stw + ((wave & 1) * 64 + 2 * q) * 512), 16, voff, 0, 0, 0);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    NS_WAIT_ALL_BARRIER();
+    tile_load(T, lo_g, ldt, wave, lane);
+    NS_WAIT_DMA_BARRIER();
 
     const bool staged = !last || M.trans;
     bf16* user = static_cast<bf16*>(M.user);
@@ -509,50 +551,42 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int q = wr * 16 + i * 4 + rg;
-                char* a = stm + (j * 32 + fr) * 512 + ((q ^ fr) << 4) + (fg << 3);
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(a);
-                float y[4];
+                const int c = wc * 128 + j * 32 + fr;
+                const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
+                bf16x4* a = reinterpret_cast<bf16x4*>(T.at(c, r0));
+                const bf16x4 lo = *a;
                 bf16x4 hi;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    y[e] = fmaf(ca, (float)lo[e], acc[i][j][rg * 4 + e]);
-                    hi[e] = (bf16)y[e];
-                    acc[i][j][rg * 4 + e] = y[e] - (float)hi[e];
+                    const float y = fmaf(ca, (float)lo[e], acc[i][j][rg * 4 + e]);
+                    hi[e] = (bf16)y;
+                    acc[i][j][rg * 4 + e] = y - (float)hi[e];
                 }
                 if (staged) {
-                    *reinterpret_cast<bf16x4*>(a) = hi;
+                    *a = hi;
                 } else {
-                    // last step, caller's buffer row-major in the oriented layout
-                    const int64_t r0 = gbi + q * 8 + fg * 4;
-                    const int64_t c = gbj + wc * 128 + j * 32 + fr;
-                    if (c < M.n) {
+                    // last step, rows <= cols: the caller's buffer is X itself
+                    const int64_t gr = gbi + r0, gc = gbj + c;
+                    if (gc < M.n) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (r0 + e < M.m)
-                                user[(r0 + e) * M.cols + c] = hi[e];
+                            if (gr + e < M.m)
+                                user[(gr + e) * M.cols + gc] = hi[e];
                     }
                 }
             }
     if (!staged)
         return;
 
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (!last) {
-        bf16* xt = static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi;
-#pragma unroll 4
-        for (int q = 0; q < 32; ++q) {
-            const int tc = wave * 64 + 2 * q + half;
-            const uint4 v = *reinterpret_cast<const uint4*>(stw + ((wave & 1) * 64 + 2 * q + half) * 512 + p * 16);
-            *reinterpret_cast<uint4*>(xt + tc * ldt + 8 * (p ^ (tc & 31))) = v;
-        }
-    } else {
+    NS_WAIT_LDS_BARRIER();
+    if (last) {
         // last step, rows > cols: the caller's buffer is X^T, rows of M.cols
+        const int half = lane >> 5, p = lane & 31;
 #pragma unroll 4
         for (int q = 0; q < 32; ++q) {
-            const int tc = wave * 64 + 2 * q + half;
-            const int64_t c = gbj + tc, r0 = gbi + 8 * (p ^ (tc & 31));
-            const uint4 v = *reinterpret_cast<const uint4*>(stw + ((wave & 1) * 64 + 2 * q + half) * 512 + p * 16);
+            const int R = wave * 64 + 2 * q + half;
+            const int64_t c = gbj + R, r0 = gbi + 8 * (p ^ (R & 31));
+            const uint4 v = *reinterpret_cast<const uint4*>(T.row(R) + p * 16);
             if (c < M.n) {
                 bf16* dst = user + c * M.cols + r0;
                 if (r0 + 8 <= M.m && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
@@ -568,36 +602,32 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st
         }
         return;
     }
-
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    tile_store(T, static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi, ldt, wave, lane);
+    NS_WAIT_LDS_BARRIER();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int q = wr * 16 + i * 4 + rg;
+                const int c = wc * 128 + j * 32 + fr;
+                const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
                 bf16x4 lo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     lo[e] = (bf16)acc[i][j][rg * 4 + e];
-                *reinterpret_cast<bf16x4*>(stm + (j * 32 + fr) * 512 + ((q ^ fr) << 4) + (fg << 3)) = lo;
+                *reinterpret_cast<bf16x4*>(T.at(c, r0)) = lo;
             }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    bf16* xlo = static_cast<bf16*>(M.xlo) + gbj * ldt + gbi;
-#pragma unroll 4
-    for (int q = 0; q < 32; ++q) {
-        const int tc = wave * 64 + 2 * q + half;
-        const uint4 v = *reinterpret_cast<const uint4*>(stw + ((wave & 1) * 64 + 2 * q + half) * 512 + p * 16);
-        *reinterpret_cast<uint4*>(xlo + tc * ldt + 8 * (p ^ (tc & 31))) = v;
-    }
+    NS_WAIT_LDS_BARRIER();
+    tile_store(T, lo_g, ldt, wave, lane);
 }
 
-template <typename OpT, int STAGE>
+template <int DT, int STAGE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
                                                       const Tile* __restrict__ tiles, int cur,
                                                       int last, float ca, float cb, float cc)
 {
+    using OpT = typename Elt<DT>::type;
     // Two LDS stages (P then Q, 32 KB each), one object each: with the k loop
     // unrolled over both, every LDS read and every DMA names its stage
     // statically, so the compiler can see that a refill does not touch the
@@ -1024,7 +1054,7 @@ template <typename OpT, int STAGE>
 hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, int cur, int last,
                          float a, float b, float c, hipStream_t stream)
 {
-    hipLaunchKernelGGL((k_gemm<OpT, STAGE>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
+    hipLaunchKernelGGL((k_gemm<IsBf16<OpT>::value ? 0 : 1, STAGE>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
                        cur, last, a, b, c);
     return hipGetLastError();
 }
@@ -1035,9 +1065,9 @@ hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps, f
                         float c, hipStream_t stream)
 {
     if (dtype == 0)
-        hipLaunchKernelGGL(k_small<bf16>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
+        hipLaunchKernelGGL(k_small<0>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
     else
-        hipLaunchKernelGGL(k_small<float>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
+        hipLaunchKernelGGL(k_small<1>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
     return hipGetLastError();
 }
 
@@ -1045,10 +1075,10 @@ hipError_t launch_norm_partial(int dtype, const LargeMat* mats, int nmats, const
                                int total_parts, float* partials, hipStream_t stream)
 {
     if (dtype == 0)
-        hipLaunchKernelGGL(k_norm_partial<bf16>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+        hipLaunchKernelGGL(k_norm_partial<0>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
                            nmats, part_prefix, partials);
     else
-        hipLaunchKernelGGL(k_norm_partial<float>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+        hipLaunchKernelGGL(k_norm_partial<1>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
                            nmats, part_prefix, partials);
     return hipGetLastError();
 }
@@ -1064,10 +1094,10 @@ hipError_t launch_prep(int dtype, const LargeMat* mats, int nmats, const int32_t
                        int total_prep, const float* inv, hipStream_t stream)
 {
     if (dtype == 0)
-        hipLaunchKernelGGL(k_prep<bf16>, dim3(total_prep), dim3(kThreads), 0, stream, mats, nmats,
+        hipLaunchKernelGGL(k_prep<0>, dim3(total_prep), dim3(kThreads), 0, stream, mats, nmats,
                            prep_prefix, inv);
     else
-        hipLaunchKernelGGL(k_prep<float>, dim3(total_prep), dim3(kThreads), 0, stream, mats, nmats,
+        hipLaunchKernelGGL(k_prep<1>, dim3(total_prep), dim3(kThreads), 0, stream, mats, nmats,
                            prep_prefix, inv);
     return hipGetLastError();
 }
@@ -1076,10 +1106,10 @@ hipError_t launch_scale_out(int dtype, const LargeMat* mats, int nmats, const in
                             int total_parts, const float* inv, hipStream_t stream)
 {
     if (dtype == 0)
-        hipLaunchKernelGGL(k_scale_out<bf16>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+        hipLaunchKernelGGL(k_scale_out<0>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
                            nmats, part_prefix, inv);
     else
-        hipLaunchKernelGGL(k_scale_out<float>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
+        hipLaunchKernelGGL(k_scale_out<1>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
                            nmats, part_prefix, inv);
     return hipGetLastError();
 }
