@@ -394,30 +394,34 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
 // each wavefront 128x128 = 4x4 MFMA blocks of 32x32 (16 fp32 accumulators
 // per lane per block).
 //
-// K advances in k-tiles of 128 bytes per row (64 bf16 / 32 fp32). A k-tile of
-// one operand is 256 rows x 128 B = 32 KB; P and Q k-tiles alternate between
-// two LDS stages (64 KB each): while k-tile kt is multiplied, kt+1 streams
-// into the other stage. Global -> LDS moves use buffer_load_dwordx4 ... lds: each
-// lane's 16 bytes land at M0 + 16 * lane, so one wavefront instruction fills
-// 1 KB of LDS, and which global chunk a lane fetches decides the LDS layout.
+// K advances in slots of 64 bytes per row (32 bf16 / 16 fp32): one slot of
+// one operand is 256 rows x 64 B = 16 KB, and P and Q slots go through a ring
+// of four LDS slots (32 KB each). While slot s is multiplied, slots s + 1 ..
+// s + 3 stream in: 96 KB of operand loads in flight per compute unit. The
+// global -> L2 -> LDS stream is latency-bound at this depth (measured: with one
+// 64 KB stage in flight it moved ~11.6 TB/s, with two ~18 TB/s), which is why
+// the ring is deep rather than the stages large. Global -> LDS moves use
+// buffer_load_dwordx4 ... lds: each lane's 16 bytes land at M0 + 16 * lane, so
+// one wavefront instruction fills 1 KB of LDS, and which global chunk a lane
+// fetches decides the LDS layout.
 //
-// LDS layout of a stage operand: row r occupies the 128 bytes at r * 128; its
-// logical 16-byte chunk c (0..7) is stored at chunk c ^ g(r), with
-// g(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7. Over any 8 consecutive rows g takes
-// 8 distinct values, and over 16 it takes 8 distinct values per row parity,
-// so the rows an MFMA operand read touches at one logical chunk (8 per
-// 128-byte bank cycle, 16 per 256-byte one) land on distinct bank groups.
+// LDS layout of a slot operand: row r occupies the 64 bytes at r * 64; its
+// logical 16-byte chunk c (0..3) is stored at chunk c ^ g(r), g(r) = (r >> 2) & 3.
+// A 16-lane group of an MFMA operand read touches 16 consecutive rows at one
+// logical chunk; rows r and r + 4j share a 64-byte bank window and g gives
+// them distinct chunks, so the group covers all 64 banks once.
 //
 // Lane l of an MFMA operand read takes row (l & 31) of its 32-row block and
 // logical chunk 2*ks + (l >> 5); A and B operands use the same (lane group,
 // element) -> k assignment, so every k meets itself.
+// (A slot holds k-steps 0 and 1.)
 //   bf16: a chunk is 8 values = one v_mfma_f32_32x32x16_bf16.
 //   fp32: a chunk is 4 values = four v_mfma_f32_32x32x2_f32, element e of both
 //         lane groups in MFMA e.
 // Accumulator register r of lane l holds row (r>>2)*8 + (l>>5)*4 + (r&3), column
 // l & 31 of the 32x32 block.
-constexpr int kStageRowBytes = 128;
-constexpr int kStageOpBytes = kTile * kStageRowBytes;   // 32 KB
+constexpr int kSlotRowBytes = 64;
+constexpr int kSlotOpBytes = kTile * kSlotRowBytes;   // 16 KB
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -442,13 +446,13 @@ template <> struct Mfma<float> {
     }
 };
 
-// Byte offset of (row r, logical chunk c) inside a stage operand.
-__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * kStageRowBytes + ((c ^ lds_swz(r)) << 4); }
+// Byte offset of (row r, logical chunk c) inside a slot operand.
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kSlotRowBytes + ((c ^ lds_swz(r)) << 4); }
 
 // X X^T on the bf16 path reads X from its transposed copy X^T (np x mp), so
-// no row-major copy of X is kept. A k-tile of an operand is then 64 rows of
-// X^T (64 k) x 256 columns (256 rows of X): 64 LDS rows of 512 bytes, the
+// no row-major copy of X is kept. A slot of an operand is then 32 rows of
+// X^T (32 k) x 256 columns (256 rows of X): 32 LDS rows of 512 bytes, the
 // 16-byte chunk c of row k stored at chunk c ^ ((k & 3) << 2).
 //
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, the 16 8-byte
@@ -468,28 +472,26 @@ __device__ __forceinline__ uint2 ds_read_tr(const char* p)
         (__attribute__((address_space(3))) v4i16*)(p)));
 }
 
-// After the K loop the two LDS stages (128 KB) hold one 256 x 256 bf16 tile
-// for the epilogues: row R (0..255) is 512 bytes at (R & 127) * 512 of st0
-// (R < 128) or st1, and its 16-byte chunk q (elements 8q .. 8q + 7) is stored
-// at chunk q ^ (R & 31). Accesses of 32 rows x one chunk (the accumulator
-// order) and of whole rows then spread over the LDS banks, and global memory
-// sees whole 512-byte rows instead of 16-byte pieces of 32 rows.
-struct LdsTile {
-    char* st0;
-    char* st1;
-    __device__ __forceinline__ char* row(int R) const { return (R < 128 ? st0 : st1) + (R & 127) * 512; }
-    // element x (0..255) of row R
-    __device__ __forceinline__ char* at(int R, int x) const
-    {
-        return row(R) + (((x >> 3) ^ (R & 31)) << 4) + (x & 7) * 2;
-    }
-};
+// After the K loop the four LDS slots (128 KB) hold one 256 x 256 bf16 tile
+// for the epilogues: row R (0..255) is 512 bytes at (R & 63) * 512 of slot
+// R >> 6, and its 16-byte chunk q (elements 8q .. 8q + 7) is stored at chunk
+// q ^ (R & 31). Accesses of 32 rows x one chunk (the accumulator order) and of
+// whole rows then spread over the LDS banks, and global memory sees whole
+// 512-byte rows instead of 16-byte pieces of 32 rows. The slots are separate
+// objects, so code picks a slot pointer by values it knows statically or per
+// wavefront, never by a per-lane row.
 
-// Whole-tile moves between an LdsTile and global rows of 256 bf16 at a pitch
-// of ld elements. Wavefront w moves rows 64w .. 64w + 63, two per instruction
-// (lanes 0-31 and 32-63), lane p = l & 31 taking stored chunk p.
-__device__ __forceinline__ void tile_load(const LdsTile& T, const bf16* src, int64_t ld, int wave,
-                                          int lane)
+// element x (0..255) of row R, R in the slot starting at `slot`
+__device__ __forceinline__ char* tile_at(char* slot, int R, int x)
+{
+    return slot + (R & 63) * 512 + (((x >> 3) ^ (R & 31)) << 4) + (x & 7) * 2;
+}
+
+// Whole-tile moves between the LDS tile and global rows of 256 bf16 at a
+// pitch of ld elements. Wavefront w moves rows 64w .. 64w + 63 (its slot
+// `ws`), two per instruction (lanes 0-31 and 32-63), lane p = l & 31 taking
+// stored chunk p.
+__device__ __forceinline__ void tile_load(char* ws, const bf16* src, int64_t ld, int wave, int lane)
 {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)src, (short)0, (int)(kTile * ld * 2), 0x00020000);
@@ -498,17 +500,17 @@ __device__ __forceinline__ void tile_load(const LdsTile& T, const bf16* src, int
     for (int q = 0; q < 32; ++q) {
         const int R = wave * 64 + 2 * q + half;
         const int voff = (int)(R * ld * 2) + ((p ^ (R & 31)) << 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)T.row(wave * 64 + 2 * q), 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(ws + 2 * q * 512), 16, voff, 0, 0, 0);
     }
 }
 
-__device__ __forceinline__ void tile_store(const LdsTile& T, bf16* dst, int64_t ld, int wave, int lane)
+__device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld, int wave, int lane)
 {
     const int half = lane >> 5, p = lane & 31;
 #pragma unroll 4
     for (int q = 0; q < 32; ++q) {
         const int R = wave * 64 + 2 * q + half;
-        const uint4 v = *reinterpret_cast<const uint4*>(T.row(R) + p * 16);
+        const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
         *reinterpret_cast<uint4*>(dst + R * ld + 8 * (p ^ (R & 31))) = v;
     }
 }
@@ -520,27 +522,31 @@ __device__ __forceinline__ void tile_store(const LdsTile& T, bf16* dst, int64_t 
 // In the epilogues, lane (fr, fg) of wavefront (wr, wc) holds, in block
 // (i, j) register 4 rg + e, tile element (r, c) with
 // r = 128 wr + 32 i + 8 rg + 4 fg + e and c = 128 wc + 32 j + fr: four
-// consecutive r of one c, i.e. 8 bytes of LdsTile row c.
+// consecutive r of one c, i.e. 8 bytes of LDS tile row c.
 
-// Epilogue of the bf16 update (X^T layout, LdsTile row = tile column c):
+// Epilogue of the bf16 update (X^T layout, LDS tile row = tile column c):
 //   X_lo tile -> LDS, y = acc + a X_lo, LDS <- bf16(y), acc <- y - bf16(y)
 //   LDS -> X_hi (next slot), LDS <- bf16(acc), LDS -> X_lo (in place)
 // Every element is read and rewritten by the same lane in the accumulator
 // passes, so only the copies need barriers. On the last step bf16(y) goes to
 // the caller's buffer instead.
-__device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st0, char* st1,
-                                                     f32x16 (&acc)[4][4], int64_t gbi, int64_t gbj,
-                                                     int nxt, int last, float ca, int wave,
-                                                     int lane)
+__device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl0, char* sl1,
+                                                     char* sl2, char* sl3, f32x16 (&acc)[4][4],
+                                                     int64_t gbi, int64_t gbj, int nxt, int last,
+                                                     float ca, int wave, int lane)
 {
     const int64_t ldt = M.ldt;
     const int fr = lane & 31, fg = lane >> 5;
     const int wr = wave >> 1, wc = wave & 1;
-    const LdsTile T{st0, st1};
     bf16* lo_g = static_cast<bf16*>(M.xlo) + gbj * ldt + gbi;
+    // this wavefront's rows in the copies; its columns 128 wc .. + 63 and
+    // 128 wc + 64 .. + 127 in the accumulator passes
+    char* ws = wave < 2 ? (wave == 0 ? sl0 : sl1) : (wave == 2 ? sl2 : sl3);
+    char* cs0 = wc ? sl2 : sl0;
+    char* cs1 = wc ? sl3 : sl1;
 
     NS_WAIT_ALL_BARRIER();
-    tile_load(T, lo_g, ldt, wave, lane);
+    tile_load(ws, lo_g, ldt, wave, lane);
     NS_WAIT_DMA_BARRIER();
 
     const bool staged = !last || M.trans;
@@ -553,7 +559,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st
             for (int rg = 0; rg < 4; ++rg) {
                 const int c = wc * 128 + j * 32 + fr;
                 const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
-                bf16x4* a = reinterpret_cast<bf16x4*>(T.at(c, r0));
+                bf16x4* a = reinterpret_cast<bf16x4*>(tile_at(j < 2 ? cs0 : cs1, c, r0));
                 const bf16x4 lo = *a;
                 bf16x4 hi;
 #pragma unroll
@@ -586,7 +592,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st
         for (int q = 0; q < 32; ++q) {
             const int R = wave * 64 + 2 * q + half;
             const int64_t c = gbj + R, r0 = gbi + 8 * (p ^ (R & 31));
-            const uint4 v = *reinterpret_cast<const uint4*>(T.row(R) + p * 16);
+            const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
             if (c < M.n) {
                 bf16* dst = user + c * M.cols + r0;
                 if (r0 + 8 <= M.m && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
@@ -602,7 +608,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st
         }
         return;
     }
-    tile_store(T, static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi, ldt, wave, lane);
+    tile_store(ws, static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi, ldt, wave, lane);
     NS_WAIT_LDS_BARRIER();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -616,10 +622,10 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* st
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     lo[e] = (bf16)acc[i][j][rg * 4 + e];
-                *reinterpret_cast<bf16x4*>(T.at(c, r0)) = lo;
+                *reinterpret_cast<bf16x4*>(tile_at(j < 2 ? cs0 : cs1, c, r0)) = lo;
             }
     NS_WAIT_LDS_BARRIER();
-    tile_store(T, lo_g, ldt, wave, lane);
+    tile_store(ws, lo_g, ldt, wave, lane);
 }
 
 template <int DT, int STAGE>
@@ -628,12 +634,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                                                       int last, float ca, float cb, float cc)
 {
     using OpT = typename Elt<DT>::type;
-    // Two LDS stages (P then Q, 32 KB each), one object each: with the k loop
-    // unrolled over both, every LDS read and every DMA names its stage
+    // Four LDS slots (P then Q, 16 KB each), one object each: with the k loop
+    // unrolled over the ring, every LDS read and every DMA names its slot
     // statically, so the compiler can see that a refill does not touch the
-    // stage being read and does not wait for it.
-    __shared__ __attribute__((aligned(1024))) char st0[2 * kStageOpBytes];
-    __shared__ __attribute__((aligned(1024))) char st1[2 * kStageOpBytes];
+    // slots being read and does not wait for them.
+    __shared__ __attribute__((aligned(1024))) char sl0[2 * kSlotOpBytes];
+    __shared__ __attribute__((aligned(1024))) char sl1[2 * kSlotOpBytes];
+    __shared__ __attribute__((aligned(1024))) char sl2[2 * kSlotOpBytes];
+    __shared__ __attribute__((aligned(1024))) char sl3[2 * kSlotOpBytes];
 
     const Tile t = tiles[blockIdx.x];
     const LargeMat& M = mats[t.mat];
@@ -660,8 +668,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         pitch = M.ldt;
     }
     const int ldb = (int)(pitch * (int64_t)sizeof(OpT));        // row pitch, bytes
-    // k-tiles: 128 bytes of K per row, or 64 rows of X^T (the same 64 bf16)
-    const int nk = (int)(K * (int64_t)sizeof(OpT) / kStageRowBytes);   // even (K % 256 == 0)
+    // slots: 64 bytes of K per row, or 32 rows of X^T (the same 32 bf16)
+    const int ns = (int)(K * (int64_t)sizeof(OpT) / kSlotRowBytes);   // a multiple of 8 (K % 256 == 0)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
@@ -679,31 +687,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     const __amdgpu_buffer_rsrc_t rq =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Q + qoff), (short)0, range_q, 0x00020000);
 
-    // DMA mapping: wavefront w fills instructions I = w + 4 q (q = 0..7) of a
-    // stage operand, 1 KB = rows 8I..8I+7 each. Lane l writes stored chunk
-    // l & 7 of row 8I + (l >> 3), i.e. logical chunk (l & 7) ^ g(row); the
-    // q offset (32 rows) leaves g unchanged.
+    // DMA mapping: wavefront w fills instructions I = w + 4 q (q = 0..3) of a
+    // slot operand, 1 KB = rows 16I..16I+15 each. Lane l writes stored chunk
+    // l & 3 of row 16I + (l >> 2), i.e. logical chunk (l & 3) ^ g(row); the
+    // q offset (64 rows) leaves g unchanged.
     // Transposed: instruction I fills LDS rows 2I, 2I+1 (k); lane l writes
     // stored chunk l & 31 of row 2I + (l >> 5); the q offset (8 rows) leaves
     // the swizzle unchanged.
-    const int dma_row = kTrans ? 2 * wave + (lane >> 5) : 8 * wave + (lane >> 3);
+    const int dma_row = kTrans ? 2 * wave + (lane >> 5) : 16 * wave + (lane >> 2);
     const int dma_voff = kTrans ? dma_row * ldb + (((lane & 31) ^ tr_swz(dma_row)) << 4)
-                                : dma_row * ldb + (((lane & 7) ^ lds_swz(dma_row)) << 4);
+                                : dma_row * ldb + (((lane & 3) ^ lds_swz(dma_row)) << 4);
 
-    // The bf16 update visits the k-tiles starting at this tile's own 256 rows
-    // (k-tile kb), wrapping around; the order is fixed per tile. Loop position
-    // kk = nk (past the end) reloads k-tile kb, which is never read.
+    // In the bf16 update, slots sb .. sb + 7 are this tile's own 256 rows.
+    // Slot positions past the end reload slot 0, which is never read.
     constexpr bool kIdent = STAGE == 2 && IsBf16<OpT>::value;
-    const int kb = kIdent ? t.bi * 4 : 0;
-    auto issue = [&](char* sp, int kk) {
-        const int kt = kk + kb >= nk ? kk + kb - nk : kk + kb;
+    const int sb = kIdent ? t.bi * 8 : 0;
+    auto issue = [&](char* sp, int s) __attribute__((always_inline)) {
+        const int ks = s < ns ? s : 0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int soff = kTrans ? (kt * 64 + 8 * q) * ldb : kt * kStageRowBytes + q * 32 * ldb;
+        for (int q = 0; q < 4; ++q) {
+            const int soff = kTrans ? (ks * 32 + 8 * q) * ldb : ks * kSlotRowBytes + q * 64 * ldb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rq, (lds_ptr_t)(sp + kStageOpBytes + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
+                rq, (lds_ptr_t)(sp + kSlotOpBytes + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
         }
     };
 
@@ -732,10 +739,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             const int ca = wr * 128 + i * 32 + 16 * (g & 1) + 4 * (x & 3);
             const int cb = wc * 128 + i * 32 + 16 * (g & 1) + 4 * (x & 3);
             aoff[i] = kr * kTrRowBytes + (((ca >> 3) ^ tr_swz(kr)) << 4) + (ca & 7) * 2;
-            boff[i] = kStageOpBytes + kr * kTrRowBytes + (((cb >> 3) ^ tr_swz(kr)) << 4) + (cb & 7) * 2;
+            boff[i] = kSlotOpBytes + kr * kTrRowBytes + (((cb >> 3) ^ tr_swz(kr)) << 4) + (cb & 7) * 2;
         } else {
             aoff[i] = lds_off(wr * 128 + i * 32 + fr, fg);
-            boff[i] = kStageOpBytes + lds_off(wc * 128 + i * 32 + fr, fg);
+            boff[i] = kSlotOpBytes + lds_off(wc * 128 + i * 32 + fr, fg);
         }
     }
     auto read_frags = [&](const char* sp, int ks, uint4 (&af)[4], uint4 (&bfr)[4]) {
@@ -761,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             for (int j = 0; j < 4; ++j)
                 Mfma<OpT>::mac(acc[i][j], af[i], bfr[j]);
     };
-    auto interleave = [] {
+    auto interleave = []() __attribute__((always_inline)) {
         // LDS reads spread between MFMAs (16 transposed 8-byte reads or 8
         // 16-byte reads per k-step)
         constexpr int nreads = kTrans ? 16 : 8;
@@ -775,23 +782,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
-    // Pipeline over two stages. Iteration kt multiplies stage `cur` (k-tile
-    // kt) while the DMA of k-tile kt+1 fills `oth`, freed by the barrier that
-    // ended iteration kt-1. Each k-step's fragments are read while the
-    // previous k-step's MFMAs run; after the last read of `cur`, the wave
-    // waits for its own DMA and passes the barrier (so `oth` is complete and
-    // nobody reads `cur` any more), reads k-step 0 of `oth` and issues the
-    // last k-step's MFMAs to cover that read.
+    // Pipeline over the ring. Step s multiplies slot s (k-steps 0 and 1) while
+    // slots s + 1 .. s + 3 are in flight: it first refills the ring position of
+    // slot s - 1 (freed by the barrier that ended step s - 1) with slot s + 3,
+    // reads k-step 1's fragments while k-step 0's MFMAs run, then waits until
+    // its own DMAs of slot s + 1 have landed (8 per slot per wavefront, so at
+    // most 16 younger ones may still run) and passes the barrier (slot s + 1
+    // complete, nobody reads slot s any more), reads k-step 0 of slot s + 1 and
+    // issues k-step 1's MFMAs to cover that read.
+    //
     // bf16 X <- aX + BX: the a X_hi part (X_hi = bf16(X), the Q operand
-    // itself) is added by the MFMAs too. Wavefront row wr holds rows
-    // 128 wr .. 128 wr + 127 of the tile, which are k-tiles 2 wr and 2 wr + 1
-    // of the first four the loop visits; there, an identity A fragment
-    // scaled by s_hi = bf16(s) and one scaled by s_lo = bf16(s - s_hi)
-    // multiply the Q fragments already in registers (k-step ks of k-tile h
-    // covers rows 16 (ks & 1) .. + 15 of 32-row block 2 (h & 1) + ks / 2).
-    // The other wavefront row adds zeros there, so the code stays straight.
-    // Those products are exact in fp32; a X_lo is added in the epilogue.
-    // (The scale a is per row: see rowscale.)
+    // itself) is added by the MFMAs too. Slots sb .. sb + 7 (sb = 8 bi) are
+    // the tile's own 256 rows; slot sb + P covers rows 32 P .. 32 P + 31, block
+    // P & 3 of wavefront row P >> 2. There an identity A fragment scaled by
+    // s_hi = bf16(s) and one scaled by s_lo = bf16(s - s_hi) multiply the Q
+    // fragments already in registers; the other wavefront row adds zeros, so
+    // the code stays straight. Those products are exact in fp32; a X_lo is
+    // added in the epilogue.
     // Per-row scale of the identity: a + (B_ii - bf16(B_ii)), which also
     // restores the part of B's diagonal that its bf16 operand dropped (the
     // diagonal dominates B when the singular values are clustered).
@@ -801,12 +808,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         for (int ii = 0; ii < 4; ++ii)
             rowscale[ii] = ca + M.bdiag[gbi + wr * 128 + ii * 32 + fr];
     }
-    auto ident = [&](int h, int ks, const uint4 (&bfr)[4]) {
-        const int ii = 2 * (h & 1) + (ks >> 1);
+    // peel slot P, k-step ks of the slot
+    auto ident = [&](int P, int ks, const uint4 (&bfr)[4]) {
+        const int ii = P & 3;
         // A fragment: lane l holds row l & 31, k = 8 (l >> 5) + e of the
-        // 32 x 16 block; the identity sits at e = (l & 31) - 16 (ks & 1) - 8 (l >> 5).
-        const int e = fr - 16 * (ks & 1) - 8 * fg;
-        const bool mine = (h >> 1) == wr;
+        // 32 x 16 block; the identity sits at e = (l & 31) - 16 ks - 8 (l >> 5).
+        const int e = fr - 16 * ks - 8 * fg;
+        const bool mine = (P >> 2) == wr;
         const bf16 ahi = (bf16)rowscale[ii];
         const bf16 alo = (bf16)(rowscale[ii] - (float)ahi);
         const uint32_t hb = mine ? __builtin_bit_cast(uint16_t, ahi) : 0u;
@@ -829,44 +837,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     };
 
     uint4 fa[4], fb[4], ga[4], gb[4];
-    // H >= 0: one of the first four k-tiles of the bf16 update (adds a X_hi)
-    auto iteration = [&](const char* cur, char* oth, int kk, auto peel) {
+    // H >= 0: slot sb + H of the bf16 update (adds a X_hi)
+    auto step = [&](const char* cur, char* refill, const char* next, int s, auto peel) __attribute__((always_inline)) {
         constexpr int H = decltype(peel)::value;
-        issue(oth, kk + 1);
+        issue(refill, s + 3);
         read_frags(cur, 1, ga, gb);
         mfma_block(fa, fb);
         interleave();
         if constexpr (H >= 0) ident(H, 0, fb);
-        read_frags(cur, 2, fa, fb);
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        read_frags(next, 0, fa, fb);
         mfma_block(ga, gb);
         interleave();
         if constexpr (H >= 0) ident(H, 1, gb);
-        read_frags(cur, 3, ga, gb);
-        mfma_block(fa, fb);
-        interleave();
-        if constexpr (H >= 0) ident(H, 2, fb);
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        read_frags(oth, 0, fa, fb);
-        mfma_block(ga, gb);
-        interleave();
-        if constexpr (H >= 0) ident(H, 3, gb);
+    };
+    // four steps from ring position 0 (slot s, s % 4 == 0)
+    auto ring = [&](int s, auto p0, auto p1, auto p2, auto p3) __attribute__((always_inline)) {
+        step(sl0, sl3, sl1, s, p0);
+        step(sl1, sl0, sl2, s + 1, p1);
+        step(sl2, sl1, sl3, s + 2, p2);
+        step(sl3, sl2, sl0, s + 3, p3);
     };
 
-    issue(st0, 0);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    read_frags(st0, 0, fa, fb);
-    int kk = 0;
+    issue(sl0, 0);
+    issue(sl1, 1);
+    issue(sl2, 2);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    read_frags(sl0, 0, fa, fb);
+    // Every tile visits the slots in the same order, so tiles that share an
+    // operand block read the same k-slice at about the same time (L2 reuse);
+    // the bf16 update's identity slots are peeled in place.
+    int s = 0;
+    for (; s < sb; s += 4)
+        ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
     if constexpr (kIdent) {
-        iteration(st0, st1, 0, Peel<0>{});
-        iteration(st1, st0, 1, Peel<1>{});
-        iteration(st0, st1, 2, Peel<2>{});
-        iteration(st1, st0, 3, Peel<3>{});
-        kk = 4;
+        ring(s, Peel<0>{}, Peel<1>{}, Peel<2>{}, Peel<3>{});
+        ring(s + 4, Peel<4>{}, Peel<5>{}, Peel<6>{}, Peel<7>{});
+        s += 8;
     }
-    for (; kk < nk; kk += 2) {
-        iteration(st0, st1, kk, Peel<-1>{});
-        iteration(st1, st0, kk + 1, Peel<-1>{});
-    }
+    for (; s < ns; s += 4)
+        ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogues. Lane l, block (i, j), register group rg holds rows
@@ -984,7 +994,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         const int nxt = cur ^ 1;
         const int64_t ldx = M.ldx, ldt = M.ldt;
         if constexpr (kIdent) {
-            update_epilogue_bf16(M, st0, st1, acc, gbi, gbj, nxt, last, ca, wave, lane);
+            update_epilogue_bf16(M, sl0, sl1, sl2, sl3, acc, gbi, gbj, nxt, last, ca, wave, lane);
             return;
         }
         // The part of aX not yet in the accumulators, per lane four rows of a
@@ -1009,7 +1019,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                     xv[j][rg] = load4(src + c * ldt + r0);
                 }
             auto group = [&](int64_t r0, int64_t c, const f32x4& x, float v0, float v1, float v2,
-                             float v3) {
+                             float v3) __attribute__((always_inline)) {
                 float y[4] = {fmaf(ca, x[0], v0), fmaf(ca, x[1], v1), fmaf(ca, x[2], v2),
                               fmaf(ca, x[3], v3)};
                 if (!last) {
