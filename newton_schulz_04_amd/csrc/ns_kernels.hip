@@ -524,14 +524,40 @@ __device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld
 // r = 128 wr + 32 i + 8 rg + 4 fg + e and c = 128 wc + 32 j + fr: four
 // consecutive r of one c, i.e. 8 bytes of LDS tile row c.
 
+// Loads rows 64 quarter .. 64 quarter + 63 of the update tile's X_lo (X^T
+// layout: row c = tile column c, 256 bf16 of rows gbi ..) into LDS slot `sp`
+// in the tile layout: 32 instructions of two rows, 8 per wavefront
+// (I = wave + 4q). Row R = 64 quarter + 2I + (l >> 5) has
+// R & 31 = (2 wave + (l >> 5)) | 8 (q & 3), so the chunk swizzle splits into a
+// per-lane part and (q & 3) << 7, and the row offset into a per-lane part and
+// a uniform one.
+__device__ __forceinline__ void issue_lo_quarter(const LargeMat& M, int64_t gbi, int64_t gbj, char* sp,
+                                                 int quarter, int wave, int lane)
+{
+    const int ldb2 = M.ldt * 2;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(M.xlo) + gbj * M.ldt + gbi), (short)0, kTile * ldb2, 0x00020000);
+    const int vrow = (lane >> 5) * ldb2;
+    const int vchunk = ((lane & 31) ^ (2 * wave + (lane >> 5))) << 4;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int I = wave + 4 * q;
+        const int soff = (quarter * 64 + 2 * I) * ldb2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sp + I * 1024), 16,
+                                                 vrow + (vchunk ^ ((q & 3) << 7)), soff, 0, 0);
+    }
+}
+
 // Epilogue of the bf16 update (X^T layout, LDS tile row = tile column c):
-//   X_lo tile -> LDS, y = acc + a X_lo, LDS <- bf16(y), acc <- y - bf16(y)
+//   X_lo tile -> LDS (three quarters already by the K loop), y = acc + a X_lo,
+//   LDS <- bf16(y), acc <- y - bf16(y)
 //   LDS -> X_hi (next slot), LDS <- bf16(acc), LDS -> X_lo (in place)
 // Every element is read and rewritten by the same lane in the accumulator
 // passes, so only the copies need barriers. On the last step bf16(y) goes to
 // the caller's buffer instead.
 __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl0, char* sl1,
-                                                     char* sl2, char* sl3, f32x16 (&acc)[4][4],
+                                                     char* sl2, char* sl3, bool lo_pre,
+                                                     f32x16 (&acc)[4][4],
                                                      int64_t gbi, int64_t gbj, int nxt, int last,
                                                      float ca, int wave, int lane)
 {
@@ -545,8 +571,16 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
     char* cs0 = wc ? sl2 : sl0;
     char* cs1 = wc ? sl3 : sl1;
 
+    // Quarters 0..2 of the X_lo tile were loaded by the K loop's last steps
+    // (lo_pre) or are loaded here; quarter 3 goes to slot 3 once every
+    // wavefront is done with the ring.
     NS_WAIT_ALL_BARRIER();
-    tile_load(ws, lo_g, ldt, wave, lane);
+    if (!lo_pre) {
+        issue_lo_quarter(M, gbi, gbj, sl0, 0, wave, lane);
+        issue_lo_quarter(M, gbi, gbj, sl1, 1, wave, lane);
+        issue_lo_quarter(M, gbi, gbj, sl2, 2, wave, lane);
+    }
+    issue_lo_quarter(M, gbi, gbj, sl3, 3, wave, lane);
     NS_WAIT_DMA_BARRIER();
 
     const bool staged = !last || M.trans;
@@ -671,7 +705,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // slots: 64 bytes of K per row, or 32 rows of X^T (the same 32 bf16)
     const int ns = (int)(K * (int64_t)sizeof(OpT) / kSlotRowBytes);   // a multiple of 8 (K % 256 == 0)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave is the same for all lanes of a wavefront; saying so keeps the
+    // values derived from it (LDS DMA targets, buffer offsets) in SGPRs
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave >> 1, wc = wave & 1;
 
     // Buffer resources over the 256-row blocks of P and Q (out-of-range reads
@@ -836,11 +873,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         }
     };
 
+    // The bf16 update's epilogue reads the tile's X_lo through LDS (row c =
+    // tile column c, 64 rows per slot). The last three steps have no operand
+    // slot left to load; they load quarters 0..2 of that X_lo tile into the
+    // ring positions they free instead (8 loads per wavefront, like a slot).
+    auto issue_lo = [&](char* sp, int quarter) __attribute__((always_inline)) {
+        issue_lo_quarter(M, gbi, gbj, sp, quarter, wave, lane);
+    };
+
     uint4 fa[4], fb[4], ga[4], gb[4];
-    // H >= 0: slot sb + H of the bf16 update (adds a X_hi)
-    auto step = [&](const char* cur, char* refill, const char* next, int s, auto peel) __attribute__((always_inline)) {
+    // H >= 0: slot sb + H of the bf16 update (adds a X_hi);
+    // L >= 0: instead of a slot, load quarter L of the update's X_lo tile
+    auto step = [&](const char* cur, char* refill, const char* next, int s, auto peel, auto lq) __attribute__((always_inline)) {
         constexpr int H = decltype(peel)::value;
-        issue(refill, s + 3);
+        constexpr int L = decltype(lq)::value;
+        if constexpr (L >= 0)
+            issue_lo(refill, L);
+        else
+            issue(refill, s + 3);
         read_frags(cur, 1, ga, gb);
         mfma_block(fa, fb);
         interleave();
@@ -853,10 +903,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     };
     // four steps from ring position 0 (slot s, s % 4 == 0)
     auto ring = [&](int s, auto p0, auto p1, auto p2, auto p3) __attribute__((always_inline)) {
-        step(sl0, sl3, sl1, s, p0);
-        step(sl1, sl0, sl2, s + 1, p1);
-        step(sl2, sl1, sl3, s + 2, p2);
-        step(sl3, sl2, sl0, s + 3, p3);
+        step(sl0, sl3, sl1, s, p0, Peel<-1>{});
+        step(sl1, sl0, sl2, s + 1, p1, Peel<-1>{});
+        step(sl2, sl1, sl3, s + 2, p2, Peel<-1>{});
+        step(sl3, sl2, sl0, s + 3, p3, Peel<-1>{});
+    };
+    // the last four steps (s = ns - 4); the refills of slots ns .. ns + 2
+    // are the X_lo quarters in the bf16 update, dummy reloads otherwise
+    auto ring_last = [&](int s, auto p0, auto p1, auto p2, auto p3) __attribute__((always_inline)) {
+        if constexpr (kIdent) {
+            step(sl0, sl3, sl1, s, p0, Peel<-1>{});
+            step(sl1, sl0, sl2, s + 1, p1, Peel<0>{});
+            step(sl2, sl1, sl3, s + 2, p2, Peel<1>{});
+            step(sl3, sl2, sl0, s + 3, p3, Peel<2>{});
+        } else {
+            ring(s, p0, p1, p2, p3);
+        }
     };
 
     issue(sl0, 0);
@@ -868,15 +930,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // operand block read the same k-slice at about the same time (L2 reuse);
     // the bf16 update's identity slots are peeled in place.
     int s = 0;
-    for (; s < sb; s += 4)
-        ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
+    bool lo_pre = false;   // X_lo quarters 0..2 already in slots 0..2
     if constexpr (kIdent) {
+        for (; s < sb; s += 4)
+            ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
         ring(s, Peel<0>{}, Peel<1>{}, Peel<2>{}, Peel<3>{});
         ring(s + 4, Peel<4>{}, Peel<5>{}, Peel<6>{}, Peel<7>{});
         s += 8;
+        for (; s + 4 < ns; s += 4)
+            ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
+        // (when the identity slots are the last ones, the epilogue loads all
+        // four quarters itself)
+        if (s < ns) {
+            ring_last(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
+            lo_pre = true;
+        }
+    } else {
+        for (; s < ns; s += 4)
+            ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
     }
-    for (; s < ns; s += 4)
-        ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogues. Lane l, block (i, j), register group rg holds rows
@@ -994,7 +1066,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         const int nxt = cur ^ 1;
         const int64_t ldx = M.ldx, ldt = M.ldt;
         if constexpr (kIdent) {
-            update_epilogue_bf16(M, sl0, sl1, sl2, sl3, acc, gbi, gbj, nxt, last, ca, wave, lane);
+            update_epilogue_bf16(M, sl0, sl1, sl2, sl3, lo_pre, acc, gbi, gbj, nxt, last, ca, wave, lane);
             return;
         }
         // The part of aX not yet in the accumulators, per lane four rows of a
