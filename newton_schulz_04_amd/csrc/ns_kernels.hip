@@ -356,6 +356,44 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
     const float s = inv[mi];
     const T* g = static_cast<const T*>(M.user);
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    if constexpr (DT == 0) {
+        if (M.trans) {
+            // bf16, rows > cols: X^T = G row for row, so no transpose. Thread
+            // t writes elements i0 + 16 (t & 3) .. + 15 of X^T row j0 + (t >> 2)
+            // (X_hi and X_lo) with 16-byte accesses where the row allows.
+            const int64_t j = j0 + (threadIdx.x >> 2);
+            const int64_t i = i0 + 16 * (threadIdx.x & 3);
+            const bf16* src = g + j * M.cols + i;
+            float v[16];
+            if (j < M.n && i + 16 <= M.m && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(src);
+                const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[e] = (float)a[e] * s;
+                    v[8 + e] = (float)b[e] * s;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    v[e] = (j < M.n && i + e < M.m) ? to_f32(src[e]) * s : 0.f;
+            }
+            bf16x8 h[2], l[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const bf16 hb = (bf16)v[e];
+                h[e >> 3][e & 7] = hb;
+                l[e >> 3][e & 7] = (bf16)(v[e] - (float)hb);
+            }
+            bf16* xt = static_cast<bf16*>(M.xt[0]) + j * M.ldt + i;
+            bf16* xl = static_cast<bf16*>(M.xlo) + j * M.ldt + i;
+            *reinterpret_cast<bf16x8*>(xt) = h[0];
+            *reinterpret_cast<bf16x8*>(xt + 8) = h[1];
+            *reinterpret_cast<bf16x8*>(xl) = l[0];
+            *reinterpret_cast<bf16x8*>(xl + 8) = l[1];
+            return;
+        }
+    }
     if (!M.trans) {
         // X[i][j] = G[i][j]: read G rows, write X direct, X^T through LDS.
         for (int p = 0; p < 16; ++p) {
