@@ -750,7 +750,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     const int wr = wave >> 1, wc = wave & 1;
 
     // Buffer resources over the 256-row blocks of P and Q (out-of-range reads
-    // would return 0; every offset used below is in range).
+    // return 0 without touching memory; only the K loop's loads past the last
+    // slot use that, see issue()).
     // (Transposed operands: the blocks are column ranges of X^T and the
     // resource spans all np rows.)
     const int64_t poff = kTrans ? (int64_t)t.bi * kTile * 2 : (int64_t)t.bi * kTile * ldb;
@@ -774,14 +775,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                                 : dma_row * ldb + (((lane & 3) ^ lds_swz(dma_row)) << 4);
 
     // In the bf16 update, slots sb .. sb + 7 are this tile's own 256 rows.
-    // Slot positions past the end reload slot 0, which is never read.
+    // Slot positions past the end (s >= ns) are loads that nobody reads but
+    // that keep the per-slot load count (and so the wait counts) uniform:
+    // their scalar offset is past the end of both resources, so they return
+    // zeros without memory traffic. (voffset < 2^29 and ranges < 2^31, so the
+    // 32-bit offset sum cannot wrap back into range.)
     constexpr bool kIdent = STAGE == 2 && IsBf16<OpT>::value;
     const int sb = kIdent ? t.bi * 8 : 0;
+    const int soff_end = range_p > range_q ? range_p : range_q;
     auto issue = [&](char* sp, int s) __attribute__((always_inline)) {
-        const int ks = s < ns ? s : 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int soff = kTrans ? (ks * 32 + 8 * q) * ldb : ks * kSlotRowBytes + q * 64 * ldb;
+            const int soff = s >= ns ? soff_end
+                                     : kTrans ? (s * 32 + 8 * q) * ldb : s * kSlotRowBytes + q * 64 * ldb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
