@@ -3,6 +3,7 @@ profiles/ (host-side parsing only; nothing here touches the GPU).
 
     python -m newton_schulz_04_amd.profiling stats KERNEL_STATS_CSV OUT_MD --command "..."
     python -m newton_schulz_04_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_JSON --command "..."
+    python -m newton_schulz_04_amd.profiling summary KERNEL_STATS_CSV TRAFFIC_JSON BENCH_JSON OUT_MD --title ... --command "..."
 
 `stats` reads the kernel statistics that `rocprofv3 --kernel-trace --stats`
 writes and tabulates the per-kernel average durations.
@@ -117,9 +118,87 @@ def stats_md(stats_csv, command):
     return "\n".join(["Command:", "", "    " + command, ""] + lines) + "\n"
 
 
+def algorithmic_bytes(shapes, elt=2):
+    """Bytes each kernel must move per launch over a batch of large bf16
+    matrices (m = min dim, n = max dim): what the definition reads and
+    writes, with no re-reads. X moves as X_hi + X_lo (2 + 2 bytes)."""
+    out = collections.Counter()
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        out["syrk read"] += 2 * n * m            # X_hi
+        out["syrk write"] += 2 * m * m           # A
+        out["poly read"] += 2 * m * m            # A
+        out["poly write"] += 2 * m * m           # B
+        out["update read"] += 2 * m * m + 4 * n * m   # B, X_hi, X_lo
+        out["update write"] += 4 * n * m         # X_hi, X_lo (next step)
+        out["prep read"] += elt * n * m
+        out["prep write"] += 4 * n * m
+        out["norm_partial read"] += elt * n * m
+    return out
+
+
+def summary_md(stats_csv, traffic_json, bench_json, title, shapes, kt_command):
+    with open(traffic_json) as f:
+        t = json.load(f)
+    with open(bench_json) as f:
+        b = json.loads(f.read().strip().splitlines()[-1])
+    alg = algorithmic_bytes(shapes)
+    ks = {k: v["ms_avg"] for k, v in b["kernels"].items()}
+    rows = ["| kernel | fetch (GB/launch) | write (GB/launch) | algorithmic read / write (GB) |",
+            "|---|---|---|---|"]
+    for k in ("update", "syrk", "poly", "prep", "norm_partial"):
+        e = t["kernels"].get(k)
+        if not e:
+            continue
+        rows.append(f"| {k} | {e['fetch_bytes'] / 1e9:.2f} | {e['write_bytes'] / 1e9:.2f} | "
+                    f"{alg[k + ' read'] / 1e9:.2f} / {alg[k + ' write'] / 1e9:.2f} |")
+    cp = t["copy_probe"]
+    return f"""# {title}
+
+One bench step = one `ns_orthogonalize_batched` call over the batch: norm_partial,
+norm_final, prep, then 5 x (syrk = `k_gemm<0, 0>` X X^T, poly = `k_gemm<0, 1>`
+bA + cA^2, update = `k_gemm<0, 2>` aX + BX). `copy_probe` rows are the runtime's
+device copies (bench restores its inputs between steps, outside the timed region).
+Run from the repository root with `export TMPDIR=/tmp` and the library built
+in-tree (`python -c "import __graft_entry__ as g; g.build()"`).
+
+## Kernel trace (rocprofv3 --kernel-trace --stats)
+
+{stats_md(stats_csv, kt_command)}
+The same run's bench line (HIP events on the launch stream): value {b['value']}
+matrices/s, {b['tflops']} TFLOP/s ({b['pct_bf16_peak']}% of 2.5 PFLOP/s); per-launch ms:
+{", ".join(f"{k} {v}" for k, v in ks.items())}.
+
+## HBM-side traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
+
+    {t['command']}
+
+The 1 GiB copy probe reads FETCH_SIZE = {cp['fetch_kib']:.0f} KiB and WRITE_SIZE =
+{cp['write_kib']:.0f} KiB, so fetch readings are scaled by {cp['fetch_scale']} and write readings by
+{cp['write_scale']}. FETCH_SIZE counts L2 misses, whether the Infinity Cache or HBM serves
+them. Per launch, averaged over a step's dispatches (the last update writes the
+caller's buffer instead of X_hi and X_lo):
+
+{chr(10).join(rows)}
+
+The record with a hash of the library sources is `{os.path.basename(traffic_json)}`;
+bench.py reports the dominant kernel's bytes as `roofline.traffic` only while
+the hash matches.
+"""
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
+    m = sub.add_parser("summary")
+    m.add_argument("stats_csv")
+    m.add_argument("traffic_json")
+    m.add_argument("bench_json")
+    m.add_argument("out")
+    m.add_argument("--title", required=True)
+    m.add_argument("--shape", default="8192x6144")
+    m.add_argument("--count", type=int, default=8)
+    m.add_argument("--command", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("out")
@@ -130,7 +209,12 @@ def main():
     t.add_argument("out")
     t.add_argument("--command", required=True)
     a = ap.parse_args()
-    if a.what == "stats":
+    if a.what == "summary":
+        r, c = (int(v) for v in a.shape.split("x"))
+        with open(a.out, "w") as f:
+            f.write(summary_md(a.stats_csv, a.traffic_json, a.bench_json, a.title, [(r, c)] * a.count,
+                               a.command))
+    elif a.what == "stats":
         with open(a.out, "w") as f:
             f.write(stats_md(a.csv, a.command))
     else:
