@@ -588,8 +588,8 @@ __device__ __forceinline__ void issue_lo_quarter(const LargeMat& M, int64_t gbi,
 
 // Epilogue of the bf16 update (X^T layout, LDS tile row = tile column c):
 //   X_lo tile -> LDS (three quarters already by the K loop), y = acc + a X_lo,
-//   LDS <- bf16(y), acc <- y - bf16(y)
-//   LDS -> X_hi (next slot), LDS <- bf16(acc), LDS -> X_lo (in place)
+//   LDS <- bf16(y), X_lo <- bf16(y - bf16(y)) (global, in place, from registers)
+//   LDS -> X_hi (next slot)
 // Every element is read and rewritten by the same lane in the accumulator
 // passes, so only the copies need barriers. On the last step bf16(y) goes to
 // the caller's buffer instead.
@@ -633,15 +633,20 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                 const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
                 bf16x4* a = reinterpret_cast<bf16x4*>(tile_at(j < 2 ? cs0 : cs1, c, r0));
                 const bf16x4 lo = *a;
-                bf16x4 hi;
+                bf16x4 hi, lo2;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y = fmaf(ca, (float)lo[e], acc[i][j][rg * 4 + e]);
                     hi[e] = (bf16)y;
-                    acc[i][j][rg * 4 + e] = y - (float)hi[e];
+                    lo2[e] = (bf16)(y - (float)hi[e]);
                 }
                 if (staged) {
                     *a = hi;
+                    // the new X_lo goes straight to this tile's own X_lo block
+                    // (its loads have landed); L2 merges the 16-byte pieces of
+                    // each column into whole lines
+                    if (!last)
+                        *reinterpret_cast<bf16x4*>(lo_g + (int64_t)c * ldt + r0) = lo2;
                 } else {
                     // last step, rows <= cols: the caller's buffer is X itself
                     const int64_t gr = gbi + r0, gc = gbj + c;
@@ -681,23 +686,6 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
         return;
     }
     tile_store(ws, static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi, ldt, wave, lane);
-    NS_WAIT_LDS_BARRIER();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int c = wc * 128 + j * 32 + fr;
-                const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
-                bf16x4 lo;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    lo[e] = (bf16)acc[i][j][rg * 4 + e];
-                *reinterpret_cast<bf16x4*>(tile_at(j < 2 ? cs0 : cs1, c, r0)) = lo;
-            }
-    NS_WAIT_LDS_BARRIER();
-    tile_store(ws, lo_g, ldt, wave, lane);
 }
 
 template <int DT, int STAGE>
