@@ -95,6 +95,29 @@ ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes,
                                    const float* coeffs, int32_t dtype,
                                    void* stream);
 
+/* Longest coefficient schedule ns_orthogonalize_batched_sched accepts. */
+#define NS_MAX_SCHEDULE_STEPS 64
+
+/*
+ * As ns_orthogonalize_batched, but step s (0-based) uses its own polynomial:
+ *
+ *   coeffs  host array of 3*steps floats; (coeffs[3s], coeffs[3s+1],
+ *           coeffs[3s+2]) are (a, b, c) of step s. May be NULL only when
+ *           steps == 0.
+ *   steps   0 .. NS_MAX_SCHEDULE_STEPS.
+ *
+ * With every triple equal to (a, b, c) the result is bit for bit that of
+ * ns_orthogonalize_batched with (a, b, c). This serves iterations whose
+ * polynomial changes from step to step, e.g. a few quintic steps followed by
+ * cubic (1.5, -0.5, 0) steps that converge to the polar factor UV^T.
+ * Errors as ns_orthogonalize_batched, plus NS_EINVAL for steps above
+ * NS_MAX_SCHEDULE_STEPS.
+ */
+ns_status ns_orthogonalize_batched_sched(void* const* ptrs, const int64_t* shapes,
+                                         int32_t count, int32_t steps,
+                                         const float* coeffs, int32_t dtype,
+                                         void* stream);
+
 /*
  * Device workspace bytes a call with these shapes and dtype needs (host-only;
  * touches no device). Same validation of shapes/count/dtype as above.

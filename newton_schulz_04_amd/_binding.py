@@ -40,6 +40,8 @@ def lib() -> ctypes.CDLL:
     L.ns_orthogonalize_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32,
                                            ctypes.POINTER(ctypes.c_float), i32, vp]
     L.ns_orthogonalize_batched.restype = ctypes.c_int
+    L.ns_orthogonalize_batched_sched.argtypes = L.ns_orthogonalize_batched.argtypes
+    L.ns_orthogonalize_batched_sched.restype = ctypes.c_int
     L.ns_workspace_bytes.argtypes = [ctypes.POINTER(i64), i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.ns_workspace_bytes.restype = ctypes.c_int
     L.ns_release_workspace.argtypes = [vp]
@@ -85,21 +87,38 @@ def compute_cost(rows: int, cols: int) -> int:
     return int(lib().ns_compute_cost(rows, cols))
 
 
+def _is_schedule(coeffs) -> bool:
+    """True for a sequence of (a, b, c) triples, False for one triple."""
+    if coeffs is None:
+        return False
+    first = list(coeffs)[0] if len(coeffs) else None
+    return first is not None and hasattr(first, "__len__")
+
+
 def orthogonalize_raw(ptrs, shapes, steps: int, coeffs, dtype: int, stream: int = 0,
                       count: Optional[int] = None) -> int:
-    """Direct call of ns_orthogonalize_batched; returns the status code.
-    `ptrs` are integers (device addresses; 0 = NULL), `shapes` (rows, cols)
-    pairs; None for either passes NULL. For contract tests."""
+    """Direct call of ns_orthogonalize_batched (one (a, b, c) triple) or of
+    ns_orthogonalize_batched_sched (a sequence of triples, one per step);
+    returns the status code. `ptrs` are integers (device addresses; 0 = NULL),
+    `shapes` (rows, cols) pairs; None for either passes NULL. For contract
+    tests."""
     n = len(shapes) if count is None else count
     p = None if ptrs is None else (ctypes.c_void_p * max(1, len(ptrs)))(*[v or None for v in ptrs])
     s = None if shapes is None else _shapes_array(shapes)
+    st = ctypes.c_void_p(stream or None)
+    if _is_schedule(coeffs):
+        flat = [float(v) for t in coeffs for v in t]
+        c = (ctypes.c_float * max(1, len(flat)))(*flat)
+        return int(lib().ns_orthogonalize_batched_sched(p, s, n, steps, c, dtype, st))
     c = None if coeffs is None else (ctypes.c_float * 3)(*coeffs)
-    return int(lib().ns_orthogonalize_batched(p, s, n, steps, c, dtype, ctypes.c_void_p(stream or None)))
+    return int(lib().ns_orthogonalize_batched(p, s, n, steps, c, dtype, st))
 
 
 def orthogonalize(tensors, steps: int = 5, coeffs=QUINTIC, stream=None):
     """Orthogonalize a list of 2-D CUDA tensors (all bf16 or all fp32) in place
-    on `stream` (default: the current stream). Returns the list."""
+    on `stream` (default: the current stream). `coeffs` is one (a, b, c)
+    triple for every step, or a sequence of `steps` triples (a schedule).
+    Returns the list."""
     import torch
     tensors = list(tensors)
     if not tensors:
@@ -125,6 +144,8 @@ def orthogonalize(tensors, steps: int = 5, coeffs=QUINTIC, stream=None):
     shapes = [tuple(t.shape) for t in tensors]
     with torch.cuda.device(dev):
         s = torch.cuda.current_stream() if stream is None else stream
+        if _is_schedule(coeffs) and len(coeffs) != steps:
+            raise ValueError("a coefficient schedule needs one (a, b, c) triple per step")
         rc = orthogonalize_raw(ptrs, shapes, steps, coeffs, code, s.cuda_stream)
     _check(rc)
     return tensors

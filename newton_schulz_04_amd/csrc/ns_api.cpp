@@ -281,7 +281,7 @@ hipError_t timed(int kind, hipStream_t stream, F&& fn)
 }
 
 ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t count, int32_t steps,
-              const float* coeffs, int32_t dtype)
+              const float* coeffs, int32_t per_step, int32_t dtype)
 {
     hipStream_t stream = c->stream;
     // Plan (or reuse) --------------------------------------------------------
@@ -352,15 +352,19 @@ ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t coun
     auto* prep_prefix = reinterpret_cast<const int32_t*>(meta + p.meta_prep_prefix);
     auto* inv = reinterpret_cast<float*>(meta + p.meta_inv);
     auto* partials = reinterpret_cast<float*>(meta + p.meta_partials);
-    const float ca = steps > 0 ? coeffs[0] : 0.f;
-    const float cb = steps > 0 ? coeffs[1] : 0.f;
-    const float cc = steps > 0 ? coeffs[2] : 0.f;
+    // step s uses coeffs[3s .. 3s + 2] when per_step, else coeffs[0 .. 2]
+    auto coef = [&](int s, int k) { return coeffs[3 * (per_step ? s : 0) + k]; };
     const int nl = (int)p.large.size();
 
     hipError_t e = hipSuccess;
     if (!p.small.empty()) {
+        ns::CoeffTable table{};
+        table.per_step = per_step;
+        for (int s = 0; s < (per_step ? steps : (steps > 0 ? 1 : 0)); ++s)
+            for (int k = 0; k < 3; ++k)
+                table.v[s][k] = coef(s, k);
         e = timed(ns::kKindSmall, stream, [&] {
-            return ns::launch_small(dtype, small, (int)p.small.size(), steps, ca, cb, cc, stream);
+            return ns::launch_small(dtype, small, (int)p.small.size(), steps, table, stream);
         });
         if (e != hipSuccess)
             return hip_fail(e, "small-matrix kernel launch");
@@ -390,6 +394,7 @@ ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t coun
     const int ns_ = (int)p.syrk_tiles.size(), nu = (int)p.update_tiles.size();
     for (int s = 0; s < steps; ++s) {
         const int cur = s & 1, last = s == steps - 1;
+        const float ca = coef(s, 0), cb = coef(s, 1), cc = coef(s, 2);
         e = timed(ns::kKindSyrk, stream, [&] {
             return ns::launch_gemm(dtype, 0, large, syrk, ns_, cur, last, ca, cb, cc, stream);
         });
@@ -411,8 +416,9 @@ ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t coun
 
 extern "C" {
 
-ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes, int32_t count,
-                                   int32_t steps, const float* coeffs, int32_t dtype, void* stream)
+static ns_status orthogonalize(void* const* ptrs, const int64_t* shapes, int32_t count,
+                               int32_t steps, const float* coeffs, int32_t per_step,
+                               int32_t dtype, void* stream)
 {
     g_last_error.clear();
     if (count < 0)
@@ -423,6 +429,9 @@ ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes, int
         return fail(NS_EINVAL, "steps must be >= 0");
     if (steps > 0 && !coeffs)
         return fail(NS_EINVAL, "coeffs must not be NULL when steps > 0");
+    if (per_step && steps > ns::kMaxScheduleSteps)
+        return fail(NS_EINVAL, "a coefficient schedule holds at most " +
+                                   std::to_string(ns::kMaxScheduleSteps) + " steps");
     if (dtype != NS_BF16 && dtype != NS_FP32)
         return fail(NS_EDTYPE, "unknown dtype " + std::to_string(dtype));
     const size_t elt = dtype == NS_BF16 ? 2 : 4;
@@ -449,7 +458,20 @@ ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes, int
         return hip_fail(e, "hipGetDevice");
     Context* c = get_context(dev, static_cast<hipStream_t>(stream));
     std::lock_guard<std::mutex> lk(c->mu);
-    return run(c, shapes, ptrs, count, steps, coeffs, dtype);
+    return run(c, shapes, ptrs, count, steps, coeffs, per_step, dtype);
+}
+
+ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes, int32_t count,
+                                   int32_t steps, const float* coeffs, int32_t dtype, void* stream)
+{
+    return orthogonalize(ptrs, shapes, count, steps, coeffs, 0, dtype, stream);
+}
+
+ns_status ns_orthogonalize_batched_sched(void* const* ptrs, const int64_t* shapes, int32_t count,
+                                         int32_t steps, const float* coeffs, int32_t dtype,
+                                         void* stream)
+{
+    return orthogonalize(ptrs, shapes, count, steps, coeffs, 1, dtype, stream);
 }
 
 ns_status ns_workspace_bytes(const int64_t* shapes, int32_t count, int32_t dtype, size_t* out_bytes)

@@ -52,6 +52,14 @@ struct LargeMat {
     float* bdiag;      // bf16 path: B_ii - bf16(B_ii), mp floats
 };
 
+// Iteration coefficients for the fused small path, passed by value: step s
+// uses row s when per_step, else row 0 for every step.
+constexpr int kMaxScheduleSteps = 64;
+struct CoeffTable {
+    float v[kMaxScheduleSteps][3];
+    int32_t per_step;
+};
+
 // One matrix of the fused small path.
 struct SmallMat {
     void* user;

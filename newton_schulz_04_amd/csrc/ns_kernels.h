@@ -11,7 +11,7 @@ namespace ns {
 // Fused whole-iteration kernel for matrices with min dim <= kSmallMax, one
 // workgroup per matrix, fp32 arithmetic.
 hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
-                        float a, float b, float c, hipStream_t stream);
+                        const CoeffTable& coeffs, hipStream_t stream);
 
 // Sum of squares of each large matrix in kNormChunk pieces (one workgroup per
 // piece) ...

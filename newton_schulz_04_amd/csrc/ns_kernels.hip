@@ -117,7 +117,7 @@ __device__ __forceinline__ int find_mat(const int32_t* prefix, int nmats, int b)
 //   X <- aX + BX column by column; thread t owns columns t, t+256, ...
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__ mats,
-                                                    int steps, float ca, float cb, float cc)
+                                                    int steps, const CoeffTable coeffs)
 {
     using T = typename Elt<DT>::type;
     __shared__ float red[4];
@@ -153,6 +153,8 @@ __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__
     const int ti = tt >> 3, tj = tt & 7;
     for (int step = 0; step < steps; ++step) {
         const bool last = step == steps - 1;
+        const float* co = coeffs.v[coeffs.per_step ? step : 0];
+        const float ca = co[0], cb = co[1], cc = co[2];
         float acc[4][4];
 #pragma unroll
         for (int p = 0; p < 4; ++p)
@@ -525,23 +527,9 @@ __device__ __forceinline__ char* tile_at(char* slot, int R, int x)
     return slot + (R & 63) * 512 + (((x >> 3) ^ (R & 31)) << 4) + (x & 7) * 2;
 }
 
-// Whole-tile moves between the LDS tile and global rows of 256 bf16 at a
-// pitch of ld elements. Wavefront w moves rows 64w .. 64w + 63 (its slot
-// `ws`), two per instruction (lanes 0-31 and 32-63), lane p = l & 31 taking
-// stored chunk p.
-__device__ __forceinline__ void tile_load(char* ws, const bf16* src, int64_t ld, int wave, int lane)
-{
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)src, (short)0, (int)(kTile * ld * 2), 0x00020000);
-    const int half = lane >> 5, p = lane & 31;
-#pragma unroll 4
-    for (int q = 0; q < 32; ++q) {
-        const int R = wave * 64 + 2 * q + half;
-        const int voff = (int)(R * ld * 2) + ((p ^ (R & 31)) << 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(ws + 2 * q * 512), 16, voff, 0, 0, 0);
-    }
-}
-
+// Whole-tile copy from the LDS tile to global rows of 256 bf16 at a pitch of
+// ld elements. Wavefront w moves rows 64w .. 64w + 63 (its slot `ws`), two
+// per instruction (lanes 0-31 and 32-63), lane p = l & 31 taking stored chunk p.
 __device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld, int wave, int lane)
 {
     const int half = lane >> 5, p = lane & 31;
@@ -1175,13 +1163,13 @@ hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, in
 
 }  // namespace
 
-hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps, float a, float b,
-                        float c, hipStream_t stream)
+hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
+                        const CoeffTable& coeffs, hipStream_t stream)
 {
     if (dtype == 0)
-        hipLaunchKernelGGL(k_small<0>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
+        hipLaunchKernelGGL(k_small<0>, dim3(count), dim3(kThreads), 0, stream, mats, steps, coeffs);
     else
-        hipLaunchKernelGGL(k_small<1>, dim3(count), dim3(kThreads), 0, stream, mats, steps, a, b, c);
+        hipLaunchKernelGGL(k_small<1>, dim3(count), dim3(kThreads), 0, stream, mats, steps, coeffs);
     return hipGetLastError();
 }
 

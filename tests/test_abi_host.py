@@ -49,6 +49,24 @@ def test_validation_without_device(kwargs, status):
         assert ns.last_error()
 
 
+def test_schedule_validation_without_device():
+    sched = [ns.QUINTIC] * 3
+    assert ns.orthogonalize_raw([0x1000], [(4, 4)], 65, [ns.QUINTIC] * 65, ns.NS_BF16) == 1
+    assert "at most 64" in ns.last_error()
+    assert ns.orthogonalize_raw([0x1000], [(4, 4)], 3, sched, 9) == 2
+    assert ns.orthogonalize_raw([0x1000], [(-1, 4)], 3, sched, ns.NS_BF16) == 1
+    # empty batches and empty matrices enqueue nothing, whatever the schedule
+    assert ns.orthogonalize_raw([0], [(0, 4)], 64, [ns.QUINTIC] * 64, ns.NS_FP32) == 0
+    lib = ns.lib()
+    # NULL coeffs with steps > 0 is rejected even for an empty batch
+    assert lib.ns_orthogonalize_batched_sched(None, None, 0, 3, None, ns.NS_BF16, None) == 1
+    assert lib.ns_orthogonalize_batched_sched(None, None, 0, 0, None, ns.NS_BF16, None) == 0
+    import ctypes
+    shp = (ctypes.c_int64 * 2)(4, 4)
+    ptr = (ctypes.c_void_p * 1)(0x1000)
+    assert lib.ns_orthogonalize_batched_sched(ptr, shp, 1, 3, None, ns.NS_BF16, None) == 1
+
+
 def test_null_coeffs_and_dtype():
     assert ns.orthogonalize_raw([0x1000], [(4, 4)], 5, None, ns.NS_BF16) == 1
     assert ns.orthogonalize_raw([0x1000], [(4, 4)], 5, ns.QUINTIC, 9) == 2

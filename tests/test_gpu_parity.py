@@ -8,7 +8,8 @@ import torch
 
 import newton_schulz_04_amd as ns
 from newton_schulz_04_amd import workloads
-from nsutil import TOL, gpu_run, oracle_run, rel_err, zero_bits
+from nsutil import TOL, coeffs32, gpu_run, oracle_run, rel_err, zero_bits
+from oracle import oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +58,43 @@ def test_large_bf16_vs_oracle(shape):
     (y,) = gpu_run([g])
     e = rel_err(y, oracle_run(g))
     assert e <= TOL[torch.bfloat16], e
+
+
+CUBIC = (1.5, -0.5, 0.0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(300, 520), (24, 300)])
+def test_constant_schedule_is_bitwise_the_plain_call(dtype, shape):
+    g = workloads.gaussian(shape, seed=21, index=shape[0], dtype=dtype)
+    (a,) = gpu_run([g], steps=5)
+    (b,) = gpu_run([g], steps=5, coeffs=[ns.QUINTIC] * 5)
+    iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(a.view(iv), b.view(iv))
+
+
+@pytest.mark.parametrize("dtype,shape", [(torch.bfloat16, (300, 520)), (torch.bfloat16, (520, 300)),
+                                         (torch.float32, (257, 300)), (torch.float32, (24, 300)),
+                                         (torch.bfloat16, (24, 2304))])
+def test_schedule_vs_oracle(dtype, shape):
+    # three quintic steps, then cubic steps toward the polar factor
+    sched = [ns.QUINTIC] * 3 + [CUBIC] * 4
+    g = workloads.gaussian(shape, seed=22, index=shape[1], dtype=dtype)
+    (y,) = gpu_run([g], steps=len(sched), coeffs=sched)
+    ref = oracle.newton_schulz(g.float().numpy(), steps=len(sched),
+                               coeffs=np.array([coeffs32(c) for c in sched]))
+    e = rel_err(y, ref)
+    assert e <= TOL[dtype], e
+
+
+def test_fp32_schedule_reaches_polar_factor():
+    # quintic steps move the spectrum into [0.68, 1.2], cubic steps then
+    # converge to U V^T (a fixed point of the cubic map)
+    g = workloads.gaussian((96, 160), seed=23, dtype=torch.float32)
+    sched = [ns.QUINTIC] * 5 + [CUBIC] * 20
+    (y,) = gpu_run([g], steps=len(sched), coeffs=sched)
+    u, _, vt = np.linalg.svd(g.double().numpy(), full_matrices=False)
+    assert rel_err(y, u @ vt) <= 1e-4
 
 
 @pytest.mark.parametrize("rank,shape", [(16, (256, 1024)), (40, (600, 300)), (1, (96, 700))])
