@@ -119,6 +119,38 @@ ns_status ns_orthogonalize_batched_sched(void* const* ptrs, const int64_t* shape
                                          void* stream);
 
 /*
+ * As ns_orthogonalize_batched, for matrices that arrive as row blocks: the
+ * row shards an all-to-all hands to the rank that orthogonalizes a matrix
+ * (microsoft/dion PR #74, "Fix megabatch_orthogonalize_async hang on empty
+ * FSDP2 shards", Summary and Fix: shards of a padded split, some of them
+ * empty; InternLM/xtuner PR #2069, the ragged exchange that sends each shard
+ * at its own length). Matrix i is the vertical concatenation of its
+ * nchunks[i] blocks; it is orthogonalized as that whole matrix and the result
+ * is written back into the same blocks, so no assembly or split copy is made.
+ * Result bits equal those of ns_orthogonalize_batched on the concatenated
+ * matrix.
+ *
+ *   chunk_ptrs  host array of sum(nchunks) device pointers, matrix 0's blocks
+ *               first, each block top to bottom. Block k holds chunk_rows[k]
+ *               rows of cols[i] elements, row-major and contiguous, aligned
+ *               to the element size; NULL only for an empty block.
+ *   chunk_rows  host array of sum(nchunks) int64 row counts, each >= 0. A
+ *               block of 0 rows (an empty shard) is never touched.
+ *   nchunks     host array of `count` int32 block counts, each >= 0.
+ *   cols        host array of `count` int64 column counts, each >= 0.
+ *   count, steps, coeffs, dtype, stream: as ns_orthogonalize_batched.
+ *
+ * Blocks must not overlap. Errors as ns_orthogonalize_batched (NS_EINVAL
+ * also for a negative block count or block row count, and for a matrix whose
+ * rows add up above 2^24).
+ */
+ns_status ns_orthogonalize_chunked(void* const* chunk_ptrs, const int64_t* chunk_rows,
+                                   const int32_t* nchunks, const int64_t* cols,
+                                   int32_t count, int32_t steps,
+                                   const float* coeffs, int32_t dtype,
+                                   void* stream);
+
+/*
  * Device workspace bytes a call with these shapes and dtype needs (host-only;
  * touches no device). Same validation of shapes/count/dtype as above.
  */

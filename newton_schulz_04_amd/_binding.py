@@ -42,6 +42,10 @@ def lib() -> ctypes.CDLL:
     L.ns_orthogonalize_batched.restype = ctypes.c_int
     L.ns_orthogonalize_batched_sched.argtypes = L.ns_orthogonalize_batched.argtypes
     L.ns_orthogonalize_batched_sched.restype = ctypes.c_int
+    L.ns_orthogonalize_chunked.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                           ctypes.POINTER(i64), i32, i32, ctypes.POINTER(ctypes.c_float),
+                                           i32, vp]
+    L.ns_orthogonalize_chunked.restype = ctypes.c_int
     L.ns_workspace_bytes.argtypes = [ctypes.POINTER(i64), i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.ns_workspace_bytes.restype = ctypes.c_int
     L.ns_release_workspace.argtypes = [vp]
@@ -149,6 +153,63 @@ def orthogonalize(tensors, steps: int = 5, coeffs=QUINTIC, stream=None):
         rc = orthogonalize_raw(ptrs, shapes, steps, coeffs, code, s.cuda_stream)
     _check(rc)
     return tensors
+
+
+def orthogonalize_chunked_raw(chunk_ptrs, chunk_rows, nchunks, cols, steps: int, coeffs,
+                              dtype: int, stream: int = 0) -> int:
+    """Direct call of ns_orthogonalize_chunked; returns the status code.
+    None for an array passes NULL. For contract tests."""
+    def arr(ctype, vals):
+        return None if vals is None else (ctype * max(1, len(vals)))(*vals)
+    p = None if chunk_ptrs is None else (ctypes.c_void_p * max(1, len(chunk_ptrs)))(
+        *[v or None for v in chunk_ptrs])
+    c = None if coeffs is None else (ctypes.c_float * 3)(*coeffs)
+    count = 0 if nchunks is None else len(nchunks)
+    return int(lib().ns_orthogonalize_chunked(p, arr(ctypes.c_int64, chunk_rows), arr(ctypes.c_int32, nchunks),
+                                              arr(ctypes.c_int64, cols), count, steps, c, dtype,
+                                              ctypes.c_void_p(stream or None)))
+
+
+def orthogonalize_chunked(matrices, steps: int = 5, coeffs=QUINTIC, stream=None):
+    """Orthogonalize matrices given as lists of row blocks (2-D CUDA tensors
+    with the matrix's column count, stacked top to bottom; blocks may have 0
+    rows) in place: each matrix is treated as the concatenation of its
+    blocks and the result lands back in them. Returns `matrices`."""
+    import torch
+    matrices = [list(m) for m in matrices]
+    blocks = [b for m in matrices for b in m]
+    if not blocks:
+        return matrices
+    dt = blocks[0].dtype
+    if dt == torch.bfloat16:
+        code = NS_BF16
+    elif dt == torch.float32:
+        code = NS_FP32
+    else:
+        raise TypeError(f"unsupported dtype {dt}; use bfloat16 or float32")
+    dev = blocks[0].device
+    cols = []
+    for m in matrices:
+        if not m:
+            cols.append(0)
+            continue
+        c = m[0].shape[1] if m[0].dim() == 2 else -1
+        for b in m:
+            if b.dim() != 2 or b.shape[1] != c:
+                raise ValueError("the blocks of a matrix must be 2-D with one column count")
+            if b.dtype != dt or b.device != dev or dev.type != "cuda":
+                raise ValueError("all blocks must share one dtype and CUDA device")
+            if b.numel() and not b.is_contiguous():
+                raise ValueError("blocks must be contiguous (row-major)")
+        cols.append(c)
+    ptrs = [b.data_ptr() if b.numel() else 0 for b in blocks]
+    rows = [b.shape[0] for b in blocks]
+    with torch.cuda.device(dev):
+        s = torch.cuda.current_stream() if stream is None else stream
+        rc = orthogonalize_chunked_raw(ptrs, rows, [len(m) for m in matrices], cols, steps, coeffs, code,
+                                       s.cuda_stream)
+    _check(rc)
+    return matrices
 
 
 def workspace_bytes(shapes, dtype: int) -> int:

@@ -18,6 +18,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -81,9 +82,23 @@ struct PinnedSlot {
     bool used = false;
 };
 
+// Where the caller's matrices live: one contiguous row-major buffer each, or
+// (chunked) a vertical stack of row blocks, matrix i taking the next
+// nchunks[i] blocks of chunk_ptrs / chunk_rows.
+struct Layout {
+    void* const* ptrs = nullptr;
+    void* const* chunk_ptrs = nullptr;
+    const int64_t* chunk_rows = nullptr;
+    const int32_t* nchunks = nullptr;
+    int32_t total_chunks = 0;
+    bool chunked() const { return chunk_ptrs != nullptr; }
+};
+
 struct CachedPlan {
     std::vector<int64_t> shapes;
-    std::vector<uintptr_t> ptrs;
+    std::vector<uintptr_t> ptrs;          // matrix or chunk pointers
+    std::vector<int64_t> chunk_rows;      // chunked calls only
+    std::vector<int32_t> nchunks;         // chunked calls only
     int32_t dtype = 0;
     void* ws_base = nullptr;
     void* meta = nullptr;          // device metadata block
@@ -191,16 +206,65 @@ PinnedSlot* get_slot(Context* c, size_t bytes, std::string* err)
 }
 
 // Host image of the metadata block [0, meta_inv).
-void build_meta(const Plan& p, void* const* ptrs, char* ws, char* meta, std::vector<char>* out)
+// Row tables of a chunked call, placed after the plan's metadata: matrix i's
+// table (rows pointers) at rowtab_off[i] of the block; returns the bytes.
+size_t rowtab_layout(const Plan& p, const Layout& L, int32_t count, std::vector<size_t>* off)
 {
-    out->assign(p.meta_inv, 0);
+    off->assign(count, SIZE_MAX);
+    if (!L.chunked())
+        return 0;
+    size_t at = (p.meta_end + 255) / 256 * 256;
+    const size_t start = at;
+    for (int32_t i = 0; i < count; ++i) {
+        const ns::PlanMat& pm = p.mats[i];
+        if (pm.rows == 0 || pm.cols == 0)
+            continue;
+        (*off)[i] = at;
+        at = (at + sizeof(void*) * (size_t)pm.rows + 255) / 256 * 256;
+    }
+    return at - start;
+}
+
+void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* meta,
+                std::vector<char>* out)
+{
+    std::vector<size_t> rt_off;
+    const size_t rt_bytes = rowtab_layout(p, L, count, &rt_off);
+    // chunked: everything up to the end of the row tables (the device-written
+    // norm and scale region in between goes up as zeros)
+    out->assign(L.chunked() ? (p.meta_end + 255) / 256 * 256 + rt_bytes : p.meta_inv, 0);
     char* h = out->data();
+    std::vector<void*> user(count, nullptr);
+    std::vector<void* const*> tab(count, nullptr);
+    if (!L.chunked()) {
+        for (int32_t i = 0; i < count; ++i)
+            user[i] = L.ptrs[i];
+    } else {
+        const size_t elt = p.elt;
+        int32_t k = 0;
+        for (int32_t i = 0; i < count; ++i) {
+            const ns::PlanMat& pm = p.mats[i];
+            void** rows = rt_off[i] == SIZE_MAX ? nullptr : reinterpret_cast<void**>(h + rt_off[i]);
+            int64_t r = 0;
+            for (int32_t q = 0; q < L.nchunks[i]; ++q, ++k) {
+                char* base = static_cast<char*>(L.chunk_ptrs[k]);
+                for (int64_t j = 0; j < L.chunk_rows[k]; ++j, ++r)
+                    if (rows)
+                        rows[r] = base + (size_t)j * pm.cols * elt;
+                if (!user[i] && L.chunk_rows[k] > 0)
+                    user[i] = base;
+            }
+            if (rows)
+                tab[i] = reinterpret_cast<void* const*>(meta + rt_off[i]);
+        }
+    }
     auto ws_at = [&](size_t off) -> void* { return off == SIZE_MAX ? nullptr : ws + off; };
     for (size_t li = 0; li < p.large.size(); ++li) {
         const ns::PlanMat& pm = p.mats[p.large[li]];
         const ns::LargeOffsets& lo = p.large_off[li];
         ns::LargeMat d{};
-        d.user = ptrs[pm.index];
+        d.user = user[pm.index];
+        d.rows_tab = tab[pm.index];
         d.rows = pm.rows;
         d.cols = pm.cols;
         d.m = pm.m;
@@ -229,7 +293,8 @@ void build_meta(const Plan& p, void* const* ptrs, char* ws, char* meta, std::vec
     for (size_t si = 0; si < p.small.size(); ++si) {
         const ns::PlanMat& pm = p.mats[p.small[si]];
         ns::SmallMat d{};
-        d.user = ptrs[pm.index];
+        d.user = user[pm.index];
+        d.rows_tab = tab[pm.index];
         d.rows = pm.rows;
         d.cols = pm.cols;
         d.m = pm.m;
@@ -247,19 +312,28 @@ void build_meta(const Plan& p, void* const* ptrs, char* ws, char* meta, std::vec
         std::memcpy(h + p.meta_update, p.update_tiles.data(), p.update_tiles.size() * sizeof(ns::Tile));
     std::memcpy(h + p.meta_part_prefix, p.part_prefix.data(), p.part_prefix.size() * sizeof(int32_t));
     std::memcpy(h + p.meta_prep_prefix, p.prep_prefix.data(), p.prep_prefix.size() * sizeof(int32_t));
-    (void)meta;
 }
 
-bool same_key(const CachedPlan& cp, const int64_t* shapes, void* const* ptrs, int32_t count,
+bool same_key(const CachedPlan& cp, const int64_t* shapes, const Layout& L, int32_t count,
               int32_t dtype, void* ws)
 {
     if (cp.dtype != dtype || cp.ws_base != ws || cp.shapes.size() != (size_t)count * 2)
         return false;
     if (std::memcmp(cp.shapes.data(), shapes, sizeof(int64_t) * 2 * count) != 0)
         return false;
-    for (int32_t i = 0; i < count; ++i)
+    if (cp.nchunks.empty() == L.chunked())
+        return false;
+    void* const* ptrs = L.chunked() ? L.chunk_ptrs : L.ptrs;
+    const size_t np_ = L.chunked() ? (size_t)L.total_chunks : (size_t)count;
+    if (cp.ptrs.size() != np_)
+        return false;
+    for (size_t i = 0; i < np_; ++i)
         if (cp.ptrs[i] != reinterpret_cast<uintptr_t>(ptrs[i]))
             return false;
+    if (L.chunked() &&
+        (std::memcmp(cp.chunk_rows.data(), L.chunk_rows, sizeof(int64_t) * np_) != 0 ||
+         std::memcmp(cp.nchunks.data(), L.nchunks, sizeof(int32_t) * count) != 0))
+        return false;
     return true;
 }
 
@@ -280,14 +354,14 @@ hipError_t timed(int kind, hipStream_t stream, F&& fn)
     return e;
 }
 
-ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t count, int32_t steps,
+ns_status run(Context* c, const int64_t* shapes, const Layout& L, int32_t count, int32_t steps,
               const float* coeffs, int32_t per_step, int32_t dtype)
 {
     hipStream_t stream = c->stream;
     // Plan (or reuse) --------------------------------------------------------
     CachedPlan* hit = nullptr;
     for (CachedPlan& cp : c->plans)
-        if (same_key(cp, shapes, ptrs, count, dtype, c->ws)) {
+        if (same_key(cp, shapes, L, count, dtype, c->ws)) {
             hit = &cp;
             break;
         }
@@ -310,19 +384,28 @@ ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t coun
         }
         CachedPlan cp;
         cp.shapes.assign(shapes, shapes + 2 * count);
-        cp.ptrs.resize(count);
-        for (int32_t i = 0; i < count; ++i)
+        void* const* ptrs = L.chunked() ? L.chunk_ptrs : L.ptrs;
+        const int32_t np_ = L.chunked() ? L.total_chunks : count;
+        cp.ptrs.resize(np_);
+        for (int32_t i = 0; i < np_; ++i)
             cp.ptrs[i] = reinterpret_cast<uintptr_t>(ptrs[i]);
+        if (L.chunked()) {
+            cp.chunk_rows.assign(L.chunk_rows, L.chunk_rows + L.total_chunks);
+            cp.nchunks.assign(L.nchunks, L.nchunks + count);
+        }
         cp.dtype = dtype;
         cp.ws_base = c->ws;
         cp.plan = plan;
-        hipError_t e = hipMallocAsync(&cp.meta, plan->meta_end, stream);
+        std::vector<size_t> rt_off;
+        const size_t rt_bytes = rowtab_layout(*plan, L, count, &rt_off);
+        const size_t meta_bytes = L.chunked() ? (plan->meta_end + 255) / 256 * 256 + rt_bytes : plan->meta_end;
+        hipError_t e = hipMallocAsync(&cp.meta, meta_bytes, stream);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(NS_ENOMEM, std::string("metadata block: ") + hipGetErrorString(e));
         }
         std::vector<char> img;
-        build_meta(*plan, ptrs, static_cast<char*>(c->ws), static_cast<char*>(cp.meta), &img);
+        build_meta(*plan, L, count, static_cast<char*>(c->ws), static_cast<char*>(cp.meta), &img);
         PinnedSlot* slot = get_slot(c, img.size(), &err);
         if (!slot) {
             (void)hipFreeAsync(cp.meta, stream);
@@ -416,15 +499,30 @@ ns_status run(Context* c, const int64_t* shapes, void* const* ptrs, int32_t coun
 
 extern "C" {
 
-static ns_status orthogonalize(void* const* ptrs, const int64_t* shapes, int32_t count,
-                               int32_t steps, const float* coeffs, int32_t per_step,
-                               int32_t dtype, void* stream)
+// Shared tail of the entry points: shapes and layout are validated.
+static ns_status submit(const int64_t* shapes, const Layout& L, int32_t count, int32_t steps,
+                        const float* coeffs, int32_t per_step, int32_t dtype, void* stream)
 {
-    g_last_error.clear();
+    bool any = false;
+    for (int32_t i = 0; i < count; ++i)
+        any = any || (shapes[2 * i] > 0 && shapes[2 * i + 1] > 0);
+    if (!any)
+        return NS_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    Context* c = get_context(dev, static_cast<hipStream_t>(stream));
+    std::lock_guard<std::mutex> lk(c->mu);
+    return run(c, shapes, L, count, steps, coeffs, per_step, dtype);
+}
+
+// Checks common to every entry point (before any shape is looked at).
+static ns_status check_common(int32_t count, int32_t steps, const float* coeffs, int32_t per_step,
+                              int32_t dtype)
+{
     if (count < 0)
         return fail(NS_EINVAL, "count must be >= 0");
-    if (count > 0 && (!ptrs || !shapes))
-        return fail(NS_EINVAL, "ptrs and shapes must not be NULL when count > 0");
     if (steps < 0)
         return fail(NS_EINVAL, "steps must be >= 0");
     if (steps > 0 && !coeffs)
@@ -434,31 +532,43 @@ static ns_status orthogonalize(void* const* ptrs, const int64_t* shapes, int32_t
                                    std::to_string(ns::kMaxScheduleSteps) + " steps");
     if (dtype != NS_BF16 && dtype != NS_FP32)
         return fail(NS_EDTYPE, "unknown dtype " + std::to_string(dtype));
+    return NS_OK;
+}
+
+static ns_status check_dims(int32_t i, int64_t r, int64_t c)
+{
+    if (r < 0 || c < 0)
+        return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a negative dimension");
+    if (r > (int64_t(1) << 24) || c > (int64_t(1) << 24))
+        return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a dimension above 2^24");
+    return NS_OK;
+}
+
+static ns_status orthogonalize(void* const* ptrs, const int64_t* shapes, int32_t count,
+                               int32_t steps, const float* coeffs, int32_t per_step,
+                               int32_t dtype, void* stream)
+{
+    g_last_error.clear();
+    ns_status st = check_common(count, steps, coeffs, per_step, dtype);
+    if (st != NS_OK)
+        return st;
+    if (count > 0 && (!ptrs || !shapes))
+        return fail(NS_EINVAL, "ptrs and shapes must not be NULL when count > 0");
     const size_t elt = dtype == NS_BF16 ? 2 : 4;
-    bool any = false;
     for (int32_t i = 0; i < count; ++i) {
         const int64_t r = shapes[2 * i], c = shapes[2 * i + 1];
-        if (r < 0 || c < 0)
-            return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a negative dimension");
-        if (r > (int64_t(1) << 24) || c > (int64_t(1) << 24))
-            return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a dimension above 2^24");
+        if ((st = check_dims(i, r, c)) != NS_OK)
+            return st;
         if (r == 0 || c == 0)
             continue;
         if (!ptrs[i])
             return fail(NS_EINVAL, "matrix " + std::to_string(i) + " is non-empty but its pointer is NULL");
         if (reinterpret_cast<uintptr_t>(ptrs[i]) % elt)
             return fail(NS_EINVAL, "matrix " + std::to_string(i) + " is not aligned to its element size");
-        any = true;
     }
-    if (!any)
-        return NS_OK;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return hip_fail(e, "hipGetDevice");
-    Context* c = get_context(dev, static_cast<hipStream_t>(stream));
-    std::lock_guard<std::mutex> lk(c->mu);
-    return run(c, shapes, ptrs, count, steps, coeffs, per_step, dtype);
+    Layout L;
+    L.ptrs = ptrs;
+    return submit(shapes, L, count, steps, coeffs, per_step, dtype, stream);
 }
 
 ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes, int32_t count,
@@ -472,6 +582,58 @@ ns_status ns_orthogonalize_batched_sched(void* const* ptrs, const int64_t* shape
                                          void* stream)
 {
     return orthogonalize(ptrs, shapes, count, steps, coeffs, 1, dtype, stream);
+}
+
+ns_status ns_orthogonalize_chunked(void* const* chunk_ptrs, const int64_t* chunk_rows,
+                                   const int32_t* nchunks, const int64_t* cols, int32_t count,
+                                   int32_t steps, const float* coeffs, int32_t dtype, void* stream)
+{
+    g_last_error.clear();
+    ns_status st = check_common(count, steps, coeffs, 0, dtype);
+    if (st != NS_OK)
+        return st;
+    if (count > 0 && (!nchunks || !cols))
+        return fail(NS_EINVAL, "nchunks and cols must not be NULL when count > 0");
+    const size_t elt = dtype == NS_BF16 ? 2 : 4;
+    std::vector<int64_t> shapes(2 * (size_t)count);
+    int64_t total = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        if (nchunks[i] < 0)
+            return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a negative chunk count");
+        total += nchunks[i];
+        if (total > std::numeric_limits<int32_t>::max())
+            return fail(NS_EINVAL, "too many chunks");
+    }
+    if (total > 0 && (!chunk_ptrs || !chunk_rows))
+        return fail(NS_EINVAL, "chunk_ptrs and chunk_rows must not be NULL when there are chunks");
+    int64_t k = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        int64_t rows = 0;
+        for (int32_t q = 0; q < nchunks[i]; ++q, ++k) {
+            const int64_t r = chunk_rows[k];
+            if (r < 0)
+                return fail(NS_EINVAL, "chunk " + std::to_string(k) + " has negative rows");
+            rows += r;
+            if (rows > (int64_t(1) << 24))
+                return fail(NS_EINVAL, "matrix " + std::to_string(i) + " has a dimension above 2^24");
+            if (r > 0 && cols[i] > 0) {
+                if (!chunk_ptrs[k])
+                    return fail(NS_EINVAL, "chunk " + std::to_string(k) + " is non-empty but its pointer is NULL");
+                if (reinterpret_cast<uintptr_t>(chunk_ptrs[k]) % elt)
+                    return fail(NS_EINVAL, "chunk " + std::to_string(k) + " is not aligned to its element size");
+            }
+        }
+        if ((st = check_dims(i, rows, cols[i])) != NS_OK)
+            return st;
+        shapes[2 * i] = rows;
+        shapes[2 * i + 1] = cols[i];
+    }
+    Layout L;
+    L.chunk_ptrs = chunk_ptrs;
+    L.chunk_rows = chunk_rows;
+    L.nchunks = nchunks;
+    L.total_chunks = (int32_t)total;
+    return submit(shapes.data(), L, count, steps, coeffs, 0, dtype, stream);
 }
 
 ns_status ns_workspace_bytes(const int64_t* shapes, int32_t count, int32_t dtype, size_t* out_bytes)

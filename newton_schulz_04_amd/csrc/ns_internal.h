@@ -33,6 +33,8 @@ enum Kind : int32_t {
 // stored zero-padded to mp x np (multiples of kTile).
 struct LargeMat {
     void* user;        // caller buffer, rows x cols row-major: G in, Y out
+    void* const* rows_tab;   // or, when not NULL, row r of G / Y is rows_tab[r]
+                             // (a matrix passed as row blocks)
     int64_t rows, cols;
     int32_t m, n;      // oriented dims
     int32_t mp, np;    // padded dims
@@ -63,6 +65,7 @@ struct CoeffTable {
 // One matrix of the fused small path.
 struct SmallMat {
     void* user;
+    void* const* rows_tab;   // as in LargeMat
     int64_t rows, cols;
     int32_t m, n, trans, batch_index;
     float* xw;         // fp32 working copy of X, m x n

@@ -49,6 +49,14 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
 __device__ __forceinline__ float to_f32(float v) { return v; }
 
+// Row r of a caller matrix: contiguous rows of `cols` elements from `user`,
+// or the row table's entry when the matrix came as row blocks.
+template <typename T>
+__device__ __forceinline__ T* grow(void* user, void* const* tab, int64_t cols, int64_t r)
+{
+    return tab ? static_cast<T*>(tab[r]) : static_cast<T*>(user) + r * cols;
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
@@ -137,14 +145,14 @@ __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__
     const int64_t numel = S.rows * S.cols;
     float s = 0.f;
     for (int64_t e = tid; e < numel; e += kThreads) {
-        const float v = to_f32(g[e]);
+        const float v = to_f32(S.rows_tab ? grow<T>(g, S.rows_tab, cols, e / cols)[e % cols] : g[e]);
         s = fmaf(v, v, s);
     }
     const float inv = 1.f / (sqrtf(block_sum(s, red)) + kEps);
 
     for (int e = tid; e < m * n; e += kThreads) {
         const int i = e / n, j = e - (e / n) * n;
-        const float v = to_f32(S.trans ? g[(int64_t)j * cols + i] : g[(int64_t)i * cols + j]);
+        const float v = to_f32(S.trans ? grow<T>(g, S.rows_tab, cols, j)[i] : grow<T>(g, S.rows_tab, cols, i)[j]);
         xw[e] = v * inv;
     }
     __syncthreads();
@@ -221,9 +229,9 @@ __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__
                     if (!last)
                         xw[r * n + j] = y;
                     else if (S.trans)
-                        g[(int64_t)j * cols + r] = from_f32<T>(y);
+                        grow<T>(g, S.rows_tab, cols, j)[r] = from_f32<T>(y);
                     else
-                        g[(int64_t)r * cols + j] = from_f32<T>(y);
+                        grow<T>(g, S.rows_tab, cols, r)[j] = from_f32<T>(y);
                 }
             }
         }
@@ -232,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__
     if (steps == 0) {
         for (int e = tid; e < m * n; e += kThreads) {
             const int i = e / n, j = e - (e / n) * n;
-            const int64_t o = S.trans ? (int64_t)j * cols + i : (int64_t)i * cols + j;
-            g[o] = from_f32<T>(xw[e]);
+            T* row = S.trans ? grow<T>(g, S.rows_tab, cols, j) : grow<T>(g, S.rows_tab, cols, i);
+            row[S.trans ? i : j] = from_f32<T>(xw[e]);
         }
     }
 }
@@ -260,7 +268,20 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const LargeMat* __res
     const T* g = static_cast<const T*>(M.user) + base;
     const int tid = threadIdx.x;
     float s = 0.f;
-    if (left >= kNormChunk && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+    if (M.rows_tab) {
+        // row blocks: the same elements in the same order, found row by row
+        for (int q = 0; q < Q; ++q) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const int64_t idx = (int64_t)(tid + kThreads * q) * V + e;
+                if (idx < left) {
+                    const int64_t flat = base + idx;
+                    const float f = to_f32(grow<const T>(nullptr, M.rows_tab, M.cols, flat / M.cols)[flat % M.cols]);
+                    s = fmaf(f, f, s);
+                }
+            }
+        }
+    } else if (left >= kNormChunk && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
         typedef T vec_t __attribute__((ext_vector_type(V)));
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -317,11 +338,13 @@ __global__ __launch_bounds__(kThreads) void k_scale_out(const LargeMat* __restri
     const LargeMat& M = mats[mi];
     const int64_t base = (int64_t)(b - prefix[mi]) * kNormChunk;
     const int64_t left = M.rows * M.cols - base;
-    T* g = static_cast<T*>(M.user) + base;
     const float s = inv[mi];
     for (int i = threadIdx.x; i < kNormChunk; i += kThreads)
-        if (i < left)
-            g[i] = from_f32<T>(to_f32(g[i]) * s);
+        if (i < left) {
+            const int64_t flat = base + i;
+            T* row = grow<T>(M.user, M.rows_tab, M.cols, flat / M.cols);
+            row[flat % M.cols] = from_f32<T>(to_f32(row[flat % M.cols]) * s);
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -365,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
             // (X_hi and X_lo) with 16-byte accesses where the row allows.
             const int64_t j = j0 + (threadIdx.x >> 2);
             const int64_t i = i0 + 16 * (threadIdx.x & 3);
-            const bf16* src = g + j * M.cols + i;
+            const bf16* src = grow<const bf16>(M.user, M.rows_tab, M.cols, j < M.n ? j : 0) + i;
             float v[16];
             if (j < M.n && i + 16 <= M.m && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(src);
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
         for (int p = 0; p < 16; ++p) {
             const int r = ty + 4 * p;
             const int64_t i = i0 + r, j = j0 + tx;
-            const float v = (i < M.m && j < M.n) ? to_f32(g[i * M.cols + j]) * s : 0.f;
+            const float v = (i < M.m && j < M.n) ? to_f32(grow<const T>(M.user, M.rows_tab, M.cols, i)[j]) * s : 0.f;
             tile[r][tx] = v;
             put_x<T>(M, i, j, v);
         }
@@ -416,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
         for (int p = 0; p < 16; ++p) {
             const int r = ty + 4 * p;
             const int64_t j = j0 + r, i = i0 + tx;
-            const float v = (i < M.m && j < M.n) ? to_f32(g[j * M.cols + i]) * s : 0.f;
+            const float v = (i < M.m && j < M.n) ? to_f32(grow<const T>(M.user, M.rows_tab, M.cols, j)[i]) * s : 0.f;
             tile[r][tx] = v;
             put_xt<T>(M, i, j, v);
         }
@@ -642,7 +665,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (gr + e < M.m)
-                                user[(gr + e) * M.cols + gc] = hi[e];
+                                grow<bf16>(user, M.rows_tab, M.cols, gr + e)[gc] = hi[e];
                     }
                 }
             }
@@ -659,7 +682,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
             const int64_t c = gbj + R, r0 = gbi + 8 * (p ^ (R & 31));
             const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
             if (c < M.n) {
-                bf16* dst = user + c * M.cols + r0;
+                bf16* dst = grow<bf16>(user, M.rows_tab, M.cols, c) + r0;
                 if (r0 + 8 <= M.m && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
                     *reinterpret_cast<uint4*>(dst) = v;
                 } else {
@@ -1132,8 +1155,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         if (r0 + e < M.m) {
-                            const int64_t o = M.trans ? c * M.cols + r0 + e : (r0 + e) * M.cols + c;
-                            user[o] = from_f32<OpT>(y[e]);
+                            OpT* row = grow<OpT>(user, M.rows_tab, M.cols, M.trans ? c : r0 + e);
+                            row[M.trans ? r0 + e : c] = from_f32<OpT>(y[e]);
                         }
                     }
                 }

@@ -67,6 +67,25 @@ def test_schedule_validation_without_device():
     assert lib.ns_orthogonalize_batched_sched(ptr, shp, 1, 3, None, ns.NS_BF16, None) == 1
 
 
+@pytest.mark.parametrize("args,status", [
+    (dict(ptrs=None, rows=None, nchunks=[], cols=[]), 0),                      # no matrices
+    (dict(ptrs=[0, 0], rows=[0, 0], nchunks=[2], cols=[2304]), 0),             # only empty shards
+    (dict(ptrs=[0x1000, 0], rows=[3, 0], nchunks=[2], cols=[0]), 0),           # zero columns
+    (dict(ptrs=[0x1000], rows=[-1], nchunks=[1], cols=[8]), 1),                # negative rows
+    (dict(ptrs=[0x1000], rows=[3], nchunks=[-1], cols=[8]), 1),                # negative chunk count
+    (dict(ptrs=[0x1000], rows=[3], nchunks=[1], cols=[-8]), 1),                # negative cols
+    (dict(ptrs=[0x1000, 0], rows=[3, 4], nchunks=[2], cols=[8]), 1),           # NULL non-empty chunk
+    (dict(ptrs=[0x1001], rows=[3], nchunks=[1], cols=[8]), 1),                 # misaligned bf16 chunk
+    (dict(ptrs=[0x1000, 0x2000], rows=[1 << 23, (1 << 23) + 1], nchunks=[2], cols=[4]), 1),  # > 2^24 rows
+    (dict(ptrs=None, rows=None, nchunks=[1], cols=[8]), 1),                    # NULL arrays with chunks
+])
+def test_chunked_validation_without_device(args, status):
+    rc = ns.orthogonalize_chunked_raw(args["ptrs"], args["rows"], args["nchunks"], args["cols"], 5,
+                                      ns.QUINTIC, ns.NS_BF16)
+    assert rc == status, ns.last_error()
+    assert ns.orthogonalize_chunked_raw([0x1000], [3], [1], [8], 5, ns.QUINTIC, 7) == 2
+
+
 def test_null_coeffs_and_dtype():
     assert ns.orthogonalize_raw([0x1000], [(4, 4)], 5, None, ns.NS_BF16) == 1
     assert ns.orthogonalize_raw([0x1000], [(4, 4)], 5, ns.QUINTIC, 9) == 2

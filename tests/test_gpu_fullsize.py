@@ -92,6 +92,17 @@ def test_ragged_remainder_batches():
     assert zero_bits(out[last.zero_rows])
     # trailing zero rows leave the real rows bitwise unchanged
     assert torch.equal(out[last.real_rows].view(torch.int16), last_unpadded.view(torch.int16))
+    # the same matrix passed as its 65 padded shards (127 rows each) and as
+    # its 65 ragged shards (64 x 127 + 64 rows), without assembling it
+    dev = last.mat.cuda()
+    ns.orthogonalize_chunked([list(dev.split(127, dim=0))])
+    torch.cuda.synchronize()
+    assert torch.equal(dev.view(torch.int16), out.view(torch.int16))
+    sizes = workloads.shard_sizes(pool[11].shape[0], 65)
+    dev = pool[11].cuda()
+    ns.orthogonalize_chunked([list(dev.split(sizes, dim=0))])
+    torch.cuda.synchronize()
+    assert torch.equal(dev.view(torch.int16), last_unpadded.view(torch.int16))
     # ragged assembly of the same shards is the original matrix
     ragged = workloads.ragged_remainder(12, world=65, padded=False)[-1].mat
     assert torch.equal(ragged, pool[11])
