@@ -604,10 +604,11 @@ __device__ __forceinline__ void issue_lo_quarter(const LargeMat& M, int64_t gbi,
 // Every element is read and rewritten by the same lane in the accumulator
 // passes, so only the copies need barriers. On the last step bf16(y) goes to
 // the caller's buffer instead.
+template <bool LAST>
 __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl0, char* sl1,
                                                      char* sl2, char* sl3, bool lo_pre,
                                                      f32x16 (&acc)[4][4],
-                                                     int64_t gbi, int64_t gbj, int nxt, int last,
+                                                     int64_t gbi, int64_t gbj, int nxt,
                                                      float ca, int wave, int lane)
 {
     const int64_t ldt = M.ldt;
@@ -632,7 +633,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
     issue_lo_quarter(M, gbi, gbj, sl3, 3, wave, lane);
     NS_WAIT_DMA_BARRIER();
 
-    const bool staged = !last || M.trans;
+    const bool staged = !LAST || M.trans;
     bf16* user = static_cast<bf16*>(M.user);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -656,7 +657,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                     // the new X_lo goes straight to this tile's own X_lo block
                     // (its loads have landed); L2 merges the 16-byte pieces of
                     // each column into whole lines
-                    if (!last)
+                    if (!LAST)
                         *reinterpret_cast<bf16x4*>(lo_g + (int64_t)c * ldt + r0) = lo2;
                 } else {
                     // last step, rows <= cols: the caller's buffer is X itself
@@ -673,7 +674,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
         return;
 
     NS_WAIT_LDS_BARRIER();
-    if (last) {
+    if (LAST) {
         // last step, rows > cols: the caller's buffer is X^T, rows of M.cols
         const int half = lane >> 5, p = lane & 31;
 #pragma unroll 4
@@ -699,7 +700,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
     tile_store(ws, static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi, ldt, wave, lane);
 }
 
-template <int DT, int STAGE>
+template <int DT, int STAGE, int LAST>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
                                                       const Tile* __restrict__ tiles, int cur,
                                                       int last, float ca, float cb, float cc)
@@ -1109,7 +1110,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         const int nxt = cur ^ 1;
         const int64_t ldx = M.ldx, ldt = M.ldt;
         if constexpr (kIdent) {
-            update_epilogue_bf16(M, sl0, sl1, sl2, sl3, lo_pre, acc, gbi, gbj, nxt, last, ca, wave, lane);
+            update_epilogue_bf16<LAST != 0>(M, sl0, sl1, sl2, sl3, lo_pre, acc, gbi, gbj, nxt, ca, wave, lane);
             return;
         }
         // The part of aX not yet in the accumulators, per lane four rows of a
@@ -1179,7 +1180,17 @@ template <typename OpT, int STAGE>
 hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, int cur, int last,
                          float a, float b, float c, hipStream_t stream)
 {
-    hipLaunchKernelGGL((k_gemm<IsBf16<OpT>::value ? 0 : 1, STAGE>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
+    // The bf16 update's last step (it writes the caller's buffer) is its own
+    // instantiation, so the other steps' epilogue carries no code for it.
+    constexpr int DT = IsBf16<OpT>::value ? 0 : 1;
+    if constexpr (STAGE == 2 && DT == 0) {
+        if (last) {
+            hipLaunchKernelGGL((k_gemm<DT, STAGE, 1>), dim3(ntiles), dim3(kThreads), 0, stream, mats,
+                               tiles, cur, last, a, b, c);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_gemm<DT, STAGE, 0>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
                        cur, last, a, b, c);
     return hipGetLastError();
 }

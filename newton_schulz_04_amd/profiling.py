@@ -43,7 +43,7 @@ def source_hash():
 
 def kernel_kind(name):
     """Short name of a kernel from its (demangled or mangled) name."""
-    m = (re.search(r"k_gemm<\s*\d+\s*,\s*(\d+)\s*>", name) or
+    m = (re.search(r"k_gemm<\s*\d+\s*,\s*(\d+)\s*(?:,\s*\d+\s*)?>", name) or
          re.search(r"k_gemmI(?:Li\d+E|DF16b|f)Li(\d+)E", name))
     if m:
         return GEMM_KINDS.get(m.group(1), "gemm" + m.group(1))
