@@ -151,6 +151,44 @@ ns_status ns_orthogonalize_chunked(void* const* chunk_ptrs, const int64_t* chunk
                                    void* stream);
 
 /*
+ * Placement of whole matrices onto `world` data-parallel ranks (host-only; no
+ * device is touched): which rank orthogonalizes each matrix and where it sits
+ * in that rank's shard of its bucket buffer. NVIDIA/Megatron-LM PR #6379,
+ * "Balance LayerWise optimizer shards by Newton-Schulz cost, not parameter
+ * size", Problem, Changes 1-3 and Notes.
+ *
+ *   numel        count element counts of the parameters as stored (a GTP
+ *                shard's local count), in backprop order.
+ *   cost         count Newton-Schulz costs of the full shapes
+ *                (ns_compute_cost of the all-gathered matrix; the element count
+ *                for a non-matrix parameter).
+ *   world        ranks (> 0); bucket_size: element threshold of a bucket
+ *                (>= 0); align: shard start alignment in elements (>= 1).
+ *   by_cost      1: largest cost first onto the rank with the least cost so far
+ *                (loads kept across buckets) among ranks whose shard stays under
+ *                1.3 x (bucket numel / world); a matrix that fits nowhere goes to
+ *                the rank with the least numel in the bucket. 0: the earlier
+ *                rule, largest numel first onto the rank with the least numel.
+ *   absorb       1: bucket_size is a soft minimum: once a bucket reaches it, a
+ *                further parameter still joins while a least-loaded placement in
+ *                backprop order puts it into existing padding. 0: a bucket
+ *                closes as soon as it reaches bucket_size.
+ *   rank, offset, bucket  count outputs: rank, element offset within that
+ *                rank's shard of the bucket, bucket index.
+ *   bucket_elems outputs per bucket (room for count entries): elements the
+ *                bucket's buffer holds, world x the largest shard.
+ *   nbuckets     output: number of buckets.
+ *   rank_cost    optional (may be NULL) world outputs: total cost per rank.
+ *
+ * Returns NS_EINVAL for negative counts/sizes/costs, world < 1, align < 1 or a
+ * NULL output; NS_OK otherwise.
+ */
+ns_status ns_plan_ranks(const int64_t* numel, const int64_t* cost, int32_t count, int32_t world,
+                        int64_t bucket_size, int64_t align, int32_t by_cost, int32_t absorb,
+                        int32_t* rank, int64_t* offset, int32_t* bucket, int64_t* bucket_elems,
+                        int32_t* nbuckets, int64_t* rank_cost);
+
+/*
  * Device workspace bytes a call with these shapes and dtype needs (host-only;
  * touches no device). Same validation of shapes/count/dtype as above.
  */

@@ -6,6 +6,6 @@ library; the first call does, and raises if it has not been built.
 """
 from ._binding import (NS_BF16, NS_FP32, QUINTIC, NSError, compute_cost,  # noqa: F401
                        last_error, lib, orthogonalize, orthogonalize_chunked,
-                       orthogonalize_chunked_raw, orthogonalize_raw, plan_classify,
+                       orthogonalize_chunked_raw, orthogonalize_raw, plan_classify, plan_ranks,
                        plan_tiles, profile_enable, profile_read, release_workspace,
                        version, workspace_bytes)

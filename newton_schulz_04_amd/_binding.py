@@ -46,6 +46,10 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(i64), i32, i32, ctypes.POINTER(ctypes.c_float),
                                            i32, vp]
     L.ns_orthogonalize_chunked.restype = ctypes.c_int
+    L.ns_plan_ranks.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, i64, i64, i32, i32,
+                                ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                ctypes.POINTER(i64), ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.ns_plan_ranks.restype = ctypes.c_int
     L.ns_workspace_bytes.argtypes = [ctypes.POINTER(i64), i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.ns_workspace_bytes.restype = ctypes.c_int
     L.ns_release_workspace.argtypes = [vp]
@@ -210,6 +214,29 @@ def orthogonalize_chunked(matrices, steps: int = 5, coeffs=QUINTIC, stream=None)
                                        s.cuda_stream)
     _check(rc)
     return matrices
+
+
+def plan_ranks(numel, cost, world: int, bucket_size: int, align: int = 1, by_cost: bool = True,
+               absorb: bool = True):
+    """ns_plan_ranks: place parameters (numel, Newton-Schulz cost; backprop
+    order) onto `world` ranks in buckets. Returns a dict with per-parameter
+    `rank`, `offset`, `bucket`, per-bucket `bucket_elems` and per-rank
+    `rank_cost`."""
+    n = len(numel)
+    if len(cost) != n:
+        raise ValueError("numel and cost must have one entry per parameter")
+    k = max(1, n)
+    rank = (ctypes.c_int32 * k)()
+    off = (ctypes.c_int64 * k)()
+    bkt = (ctypes.c_int32 * k)()
+    be = (ctypes.c_int64 * k)()
+    nb = ctypes.c_int32(0)
+    rc_ = (ctypes.c_int64 * max(1, world))()
+    _check(lib().ns_plan_ranks((ctypes.c_int64 * k)(*numel), (ctypes.c_int64 * k)(*cost), n, world,
+                               bucket_size, align, int(by_cost), int(absorb), rank, off, bkt, be,
+                               ctypes.byref(nb), rc_))
+    return {"rank": list(rank)[:n], "offset": list(off)[:n], "bucket": list(bkt)[:n],
+            "bucket_elems": list(be)[:nb.value], "rank_cost": list(rc_)[:world]}
 
 
 def workspace_bytes(shapes, dtype: int) -> int:
