@@ -418,6 +418,46 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
             *reinterpret_cast<bf16x8*>(xl + 8) = l[1];
             return;
         }
+        // bf16, rows <= cols: X = G, X^T through the LDS tile. Thread t reads
+        // 16 consecutive elements of G row i0 + (t >> 2) (16-byte loads where
+        // the row allows) and later writes 16 consecutive elements of X^T row
+        // j0 + (t >> 2); the column reads tile[16 q + e][jj] hit 64 distinct
+        // banks across a wavefront (row pitch 65 floats).
+        {
+            const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+            const int64_t i = i0 + r, j = j0 + 16 * q;
+            const bf16* src = grow<const bf16>(M.user, M.rows_tab, M.cols, i < M.m ? i : 0) + j;
+            if (i < M.m && j + 16 <= M.n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(src);
+                const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    tile[r][16 * q + e] = (float)a[e] * s;
+                    tile[r][16 * q + 8 + e] = (float)b[e] * s;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    tile[r][16 * q + e] = (i < M.m && j + e < M.n) ? to_f32(src[e]) * s : 0.f;
+            }
+            __syncthreads();
+            bf16x8 h[2], l[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float v = tile[16 * q + e][r];
+                const bf16 hb = (bf16)v;
+                h[e >> 3][e & 7] = hb;
+                l[e >> 3][e & 7] = (bf16)(v - (float)hb);
+            }
+            const int64_t jt = j0 + r, it = i0 + 16 * q;   // X^T row, first element
+            bf16* xt = static_cast<bf16*>(M.xt[0]) + jt * M.ldt + it;
+            bf16* xl = static_cast<bf16*>(M.xlo) + jt * M.ldt + it;
+            *reinterpret_cast<bf16x8*>(xt) = h[0];
+            *reinterpret_cast<bf16x8*>(xt + 8) = h[1];
+            *reinterpret_cast<bf16x8*>(xl) = l[0];
+            *reinterpret_cast<bf16x8*>(xl + 8) = l[1];
+            return;
+        }
     }
     if (!M.trans) {
         // X[i][j] = G[i][j]: read G rows, write X direct, X^T through LDS.
