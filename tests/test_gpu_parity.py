@@ -241,3 +241,49 @@ def test_contract_errors_leave_buffers_untouched():
     assert ns.orthogonalize_raw([], [], 5, ns.QUINTIC, ns.NS_FP32) == 0
     torch.cuda.synchronize()
     assert bool((canary == 7.0).all())
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(32, 2304), (33, 2304), (2304, 32), (2304, 33)])
+def test_small_large_boundary(dtype, shape):
+    # m = 32 is the last fused small-path size, m = 33 the first tiled one
+    g = workloads.gaussian(shape, seed=41, index=shape[0], dtype=dtype)
+    (y,) = gpu_run([g])
+    assert rel_err(y, oracle_run(g)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("shape", [(520, 300), (300, 520)])
+def test_unaligned_base_pointer(shape):
+    # a matrix starting 2 bytes past a 16-byte boundary takes the element-wise
+    # load paths and must give the bits of an aligned copy
+    g = workloads.gaussian(shape, seed=42, index=shape[0])
+    buf = torch.zeros(g.numel() + 16, dtype=g.dtype, device="cuda")
+    view = buf[1:1 + g.numel()].view(shape)
+    view.copy_(g.cuda())
+    ref = g.cuda().contiguous()
+    ns.orthogonalize([view, ref])
+    torch.cuda.synchronize()
+    assert torch.equal(view.view(torch.int16), ref.view(torch.int16))
+    assert buf[0].item() == 0 and not bool(buf[1 + g.numel():].view(torch.int16).any())
+
+
+@pytest.mark.parametrize("shape", [(24, 300), (300, 520)])
+def test_nan_propagates(shape):
+    # NaN and Inf are not checked: a NaN input element makes the norm, hence
+    # every output element, NaN; the call itself completes normally
+    g = workloads.gaussian(shape, seed=43)
+    g[3, 5] = float("nan")
+    (y,) = gpu_run([g])
+    assert bool(torch.isnan(y.float()).all())
+
+
+def test_many_small_matrices_one_call():
+    shapes = [(r, c) for r in (1, 7, 18, 24, 32) for c in (32, 100, 2304)] * 20
+    gs = [workloads.gaussian(s, seed=44, index=i) for i, s in enumerate(shapes)]
+    ys = gpu_run(gs)
+    for i in range(0, len(gs), 37):
+        assert rel_err(ys[i], oracle_run(gs[i])) <= TOL[torch.bfloat16]
+    # results do not depend on the batch
+    for i in (0, 150, 299):
+        (alone,) = gpu_run([gs[i]])
+        assert torch.equal(alone.view(torch.int16), ys[i].view(torch.int16))
