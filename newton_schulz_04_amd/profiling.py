@@ -156,8 +156,9 @@ def summary_md(stats_csv, traffic_json, bench_json, title, shapes, kt_command):
     return f"""# {title}
 
 One bench step = one `ns_orthogonalize_batched` call over the batch: norm_partial,
-norm_final, prep, then 5 x (syrk = `k_gemm<0, 0>` X X^T, poly = `k_gemm<0, 1>`
-bA + cA^2, update = `k_gemm<0, 2>` aX + BX). `copy_probe` rows are the runtime's
+norm_final, prep, then 5 x (syrk = `k_gemm<0, 0, 0>` X X^T, poly = `k_gemm<0, 1, 0>`
+bA + cA^2, update = `k_gemm<0, 2, 0>` aX + BX; the fifth update is `k_gemm<0, 2, 1>`,
+which writes the caller's buffer). `copy_probe` rows are the runtime's
 device copies (bench restores its inputs between steps, outside the timed region).
 Run from the repository root with `export TMPDIR=/tmp` and the library built
 in-tree (`python -c "import __graft_entry__ as g; g.build()"`).
