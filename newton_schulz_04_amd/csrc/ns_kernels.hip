@@ -621,7 +621,7 @@ __device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld
 // per-lane part and (q & 3) << 7, and the row offset into a per-lane part and
 // a uniform one.
 __device__ __forceinline__ void issue_lo_quarter(const LargeMat& M, int64_t gbi, int64_t gbj, char* sp,
-                                                 int quarter, int wave, int lane)
+                                                 int quarter, int wave, int lane, int q0 = 0, int q1 = 8)
 {
     const int ldb2 = M.ldt * 2;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -629,7 +629,7 @@ __device__ __forceinline__ void issue_lo_quarter(const LargeMat& M, int64_t gbi,
     const int vrow = (lane >> 5) * ldb2;
     const int vchunk = ((lane & 31) ^ (2 * wave + (lane >> 5))) << 4;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = q0; q < q1; ++q) {
         const int I = wave + 4 * q;
         const int soff = (quarter * 64 + 2 * I) * ldb2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sp + I * 1024), 16,
@@ -823,9 +823,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     constexpr bool kIdent = STAGE == 2 && IsBf16<OpT>::value;
     const int sb = kIdent ? t.bi * 8 : 0;
     const int soff_end = range_p > range_q ? range_p : range_q;
-    auto issue = [&](char* sp, int s) __attribute__((always_inline)) {
+    auto issue = [&](char* sp, int s, int q0 = 0, int q1 = 4) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = q0; q < q1; ++q) {
             const int soff = s >= ns ? soff_end
                                      : kTrans ? (s * 32 + 8 * q) * ldb : s * kSlotRowBytes + q * 64 * ldb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -890,27 +890,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                 Mfma<OpT>::mac(acc[i][j], af[i], bfr[j]);
     };
     auto interleave = []() __attribute__((always_inline)) {
-        // LDS reads spread between MFMAs (16 transposed 8-byte reads or 8
-        // 16-byte reads per k-step)
+        // Per k-step: the 16 MFMAs with the LDS reads of the next k-step
+        // (16 transposed 8-byte reads or 8 16-byte reads) and half of the
+        // refill's DMAs (4) spread between them. Issued in one burst, the
+        // DMAs stall the wavefront at issue while the memory pipeline is
+        // full, and that pipeline then runs dry during the MFMAs.
         constexpr int nreads = kTrans ? 16 : 8;
-        constexpr int per = kTrans ? 1 : 1;
 #pragma unroll
-        for (int q = 0; q < nreads; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+        for (int q = 0; q < 16; ++q) {
+            if (q % 4 == 0)
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if (q < nreads)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        if (!kTrans)
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
     // Pipeline over the ring. Step s multiplies slot s (k-steps 0 and 1) while
-    // slots s + 1 .. s + 3 are in flight: it first refills the ring position of
-    // slot s - 1 (freed by the barrier that ended step s - 1) with slot s + 3,
-    // reads k-step 1's fragments while k-step 0's MFMAs run, then waits until
-    // its own DMAs of slot s + 1 have landed (8 per slot per wavefront, so at
-    // most 16 younger ones may still run) and passes the barrier (slot s + 1
-    // complete, nobody reads slot s any more), reads k-step 0 of slot s + 1 and
-    // issues k-step 1's MFMAs to cover that read.
+    // slots s + 1 .. s + 3 are in flight: it refills the ring position of slot
+    // s - 1 (freed by the barrier that ended step s - 1) with slot s + 3, four
+    // of the eight DMAs per wavefront between each k-step's MFMAs. It reads
+    // k-step 1's fragments while k-step 0's MFMAs run, then waits until its
+    // own DMAs of slot s + 1 have landed (younger: the 8 of slot s + 2 and the
+    // first 4 of slot s + 3) and passes the barrier (slot s + 1 complete,
+    // nobody reads slot s any more), reads k-step 0 of slot s + 1 and issues
+    // k-step 1's MFMAs to cover that read.
     //
     // bf16 X <- aX + BX: the a X_hi part (X_hi = bf16(X), the Q operand
     // itself) is added by the MFMAs too. Slots sb .. sb + 7 (sb = 8 bi) are
@@ -961,8 +965,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // tile column c, 64 rows per slot). The last three steps have no operand
     // slot left to load; they load quarters 0..2 of that X_lo tile into the
     // ring positions they free instead (8 loads per wavefront, like a slot).
-    auto issue_lo = [&](char* sp, int quarter) __attribute__((always_inline)) {
-        issue_lo_quarter(M, gbi, gbj, sp, quarter, wave, lane);
+    auto issue_lo = [&](char* sp, int quarter, int q0, int q1) __attribute__((always_inline)) {
+        issue_lo_quarter(M, gbi, gbj, sp, quarter, wave, lane, q0, q1);
     };
 
     uint4 fa[4], fb[4], ga[4], gb[4];
@@ -972,14 +976,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         constexpr int H = decltype(peel)::value;
         constexpr int L = decltype(lq)::value;
         if constexpr (L >= 0)
-            issue_lo(refill, L);
+            issue_lo(refill, L, 0, 4);
         else
-            issue(refill, s + 3);
+            issue(refill, s + 3, 0, 2);
         read_frags(cur, 1, ga, gb);
         mfma_block(fa, fb);
         interleave();
         if constexpr (H >= 0) ident(H, 0, fb);
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // slot s + 1 complete: younger are slot s + 2 and half of s + 3
+        asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if constexpr (L >= 0)
+            issue_lo(refill, L, 4, 8);
+        else
+            issue(refill, s + 3, 2, 4);
         read_frags(next, 0, fa, fb);
         mfma_block(ga, gb);
         interleave();
