@@ -613,19 +613,20 @@ __device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld
 // r = 128 wr + 32 i + 8 rg + 4 fg + e and c = 128 wc + 32 j + fr: four
 // consecutive r of one c, i.e. 8 bytes of LDS tile row c.
 
-// Loads rows 64 quarter .. 64 quarter + 63 of the update tile's X_lo (X^T
-// layout: row c = tile column c, 256 bf16 of rows gbi ..) into LDS slot `sp`
-// in the tile layout: 32 instructions of two rows, 8 per wavefront
-// (I = wave + 4q). Row R = 64 quarter + 2I + (l >> 5) has
-// R & 31 = (2 wave + (l >> 5)) | 8 (q & 3), so the chunk swizzle splits into a
-// per-lane part and (q & 3) << 7, and the row offset into a per-lane part and
-// a uniform one.
-__device__ __forceinline__ void issue_lo_quarter(const LargeMat& M, int64_t gbi, int64_t gbj, char* sp,
-                                                 int quarter, int wave, int lane, int q0 = 0, int q1 = 8)
+// Loads rows 64 quarter .. 64 quarter + 63 of a 256 x 256 bf16 block (row c =
+// tile column c: the update's X_lo in the X^T layout, or the mirrored block of
+// the symmetric A for bA + cA^2) into LDS slot `sp` in the tile layout: 32
+// instructions of two rows, 8 per wavefront (I = wave + 4q). Row
+// R = 64 quarter + 2I + (l >> 5) has R & 31 = (2 wave + (l >> 5)) | 8 (q & 3),
+// so the chunk swizzle splits into a per-lane part and (q & 3) << 7, and the
+// row offset into a per-lane part and a uniform one. `blk` points at the
+// block's first element; rows are ld elements apart.
+__device__ __forceinline__ void issue_blk_quarter(const bf16* blk, int64_t ld, char* sp, int quarter, int wave,
+                                                  int lane, int q0 = 0, int q1 = 8)
 {
-    const int ldb2 = M.ldt * 2;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(static_cast<const bf16*>(M.xlo) + gbj * M.ldt + gbi), (short)0, kTile * ldb2, 0x00020000);
+    const int ldb2 = (int)ld * 2;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, kTile * ldb2, 0x00020000);
     const int vrow = (lane >> 5) * ldb2;
     const int vchunk = ((lane & 31) ^ (2 * wave + (lane >> 5))) << 4;
 #pragma unroll
@@ -638,7 +639,8 @@ __device__ __forceinline__ void issue_lo_quarter(const LargeMat& M, int64_t gbi,
 }
 
 // Epilogue of the bf16 update (X^T layout, LDS tile row = tile column c):
-//   X_lo tile -> LDS (three quarters already by the K loop), y = acc + a X_lo,
+//   X_lo tile -> LDS (quarter 3 in its own slot, loaded before the K loop;
+//   quarters 0..2 by the K loop's last steps), y = acc + a X_lo,
 //   LDS <- bf16(y), X_lo <- bf16(y - bf16(y)) (global, in place, from registers)
 //   LDS -> X_hi (next slot)
 // Every element is read and rewritten by the same lane in the accumulator
@@ -662,21 +664,31 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
     char* cs1 = wc ? sl3 : sl1;
 
     // Quarters 0..2 of the X_lo tile were loaded by the K loop's last steps
-    // (lo_pre) or are loaded here; quarter 3 goes to slot 3 once every
-    // wavefront is done with the ring.
+    // (lo_pre) or are loaded here, once every wavefront is done with the
+    // ring; quarter 3 (slot sl3, outside the ring) was loaded before the loop.
     NS_WAIT_ALL_BARRIER();
     if (!lo_pre) {
-        issue_lo_quarter(M, gbi, gbj, sl0, 0, wave, lane);
-        issue_lo_quarter(M, gbi, gbj, sl1, 1, wave, lane);
-        issue_lo_quarter(M, gbi, gbj, sl2, 2, wave, lane);
+        const bf16* blk = static_cast<const bf16*>(M.xlo) + gbj * ldt + gbi;
+        issue_blk_quarter(blk, ldt, sl0, 0, wave, lane);
+        issue_blk_quarter(blk, ldt, sl1, 1, wave, lane);
+        issue_blk_quarter(blk, ldt, sl2, 2, wave, lane);
+        NS_WAIT_DMA_BARRIER();
     }
-    issue_lo_quarter(M, gbi, gbj, sl3, 3, wave, lane);
-    NS_WAIT_DMA_BARRIER();
 
     const bool staged = !LAST || M.trans;
     bf16* user = static_cast<bf16*>(M.user);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        // The 16 reads of a block row go out together: the writes below could
+        // alias them as far as the compiler knows, so reads interleaved with
+        // writes would each wait out the LDS latency.
+        bf16x4 los[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+                los[j][rg] = *reinterpret_cast<const bf16x4*>(
+                    tile_at(j < 2 ? cs0 : cs1, wc * 128 + j * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -684,7 +696,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                 const int c = wc * 128 + j * 32 + fr;
                 const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
                 bf16x4* a = reinterpret_cast<bf16x4*>(tile_at(j < 2 ? cs0 : cs1, c, r0));
-                const bf16x4 lo = *a;
+                const bf16x4 lo = los[j][rg];
                 bf16x4 hi, lo2;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -710,6 +722,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                     }
                 }
             }
+    }
     if (!staged)
         return;
 
@@ -740,6 +753,173 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
     tile_store(ws, static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi, ldt, wave, lane);
 }
 
+// Epilogue of the bf16 symmetric products A = X X^T (STAGE 0) and
+// B = bA + cA^2 (STAGE 1) on tile (bi, bj), bi <= bj. Both blocks (bi, bj) and
+// (bj, bi) of the output are written, as whole 512-byte rows from the LDS
+// tile (slots s0..s3, 64 rows each):
+//   1. LDS row = tile column c (the accumulator order, 8 bytes per lane and
+//      register group; for STAGE 1 the same places hold the block of A read
+//      by the K loop's last steps, A[c][r] = A[r][c]) -> block (bj, bi).
+//   2. LDS row = tile row r -> block (bi, bj). Lanes fr and fr ^ 1 hold
+//      adjacent columns of the same four rows; one exchange of a dword gives
+//      each of them two rows of a column pair, written as 4-byte pieces.
+// On a diagonal tile only the upper triangle is used: pass 1 writes each
+// upper element at both (c, r) and (r, c), so the block is exactly symmetric,
+// and pass 2 is not needed. The diagonal keeps its bf16 rounding residue
+// (d_i = v_ii - bf16(v_ii)), and for B the first-order terms of A's residue:
+// B_ij = (b + c (dA_i + dA_j)) A_ij + c (A A)_ij, plus b dA_i on the diagonal.
+template <int STAGE>
+__device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, char* s1, char* s2, char* s3,
+                                                  f32x16 (&acc)[4][4], int64_t gbi, int64_t gbj, bool diag,
+                                                  float cb, float cc, int wave, int lane)
+{
+    const int64_t ld = M.ldt;
+    const int fr = lane & 31, fg = lane >> 5;
+    const int wr = wave >> 1, wc = wave & 1;
+    bf16* out = static_cast<bf16*>(STAGE == 0 ? M.a : M.b);
+    float* dout = STAGE == 0 ? M.adiag : M.bdiag;
+    char* ws = wave < 2 ? (wave == 0 ? s0 : s1) : (wave == 2 ? s2 : s3);
+    // pass 1: tile column c lives in slot c >> 6 = 2 wc + (j >> 1)
+    char* cs0 = wc ? s2 : s0;
+    char* cs1 = wc ? s3 : s1;
+    // pass 2 (and the mirrored writes of a diagonal tile): tile row r lives
+    // in slot r >> 6 = 2 wr + (i >> 1)
+    char* rs0 = wr ? s2 : s0;
+    char* rs1 = wr ? s3 : s1;
+
+    // A's diagonal residues at this lane's rows and columns, all requested
+    // at once (they cross the barrier below in flight)
+    float dcol[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 drows[4][4];
+    if constexpr (STAGE == 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dcol[j] = M.adiag[gbj + wc * 128 + j * 32 + fr];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+                drows[i][rg] =
+                    *reinterpret_cast<const f32x4*>(M.adiag + gbi + wr * 128 + i * 32 + rg * 8 + fg * 4);
+    }
+    // Every wavefront is done with the ring; each has waited for its own
+    // block loads (STAGE 1) at the end of the K loop.
+    NS_WAIT_LDS_BARRIER();
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 (&drow)[4] = drows[i];
+        // (A's 16 reads of a block row go out together, ahead of the writes
+        // that the compiler cannot tell apart from them)
+        bf16x4 as[4][4];
+        if constexpr (STAGE == 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg)
+                    as[j][rg] = *reinterpret_cast<const bf16x4*>(
+                        tile_at(j < 2 ? cs0 : cs1, wc * 128 + j * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c = wc * 128 + j * 32 + fr;
+                const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
+                char* cslot = j < 2 ? cs0 : cs1;
+                bf16x4* loc = reinterpret_cast<bf16x4*>(tile_at(cslot, c, r0));
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = acc[i][j][rg * 4 + e];
+                if constexpr (STAGE == 1) {
+                    const bf16x4 a = as[j][rg];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float ce = fmaf(cc, drow[rg][e] + dcol[j], cb);
+                        v[e] = ce * (float)a[e] + cc * v[e];
+                    }
+                }
+                if (!diag) {
+                    bf16x4 h;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        h[e] = (bf16)v[e];
+                    *loc = h;
+                } else {
+                    char* rslot = i < 2 ? rs0 : rs1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = r0 + e;
+                        if (r <= c) {
+                            float x = v[e];
+                            if (r == c) {
+                                if constexpr (STAGE == 1)
+                                    x = fmaf(cb, drow[rg][e], x);
+                                dout[gbi + c] = x - (float)(bf16)x;
+                            }
+                            const bf16 h = (bf16)x;
+                            *reinterpret_cast<bf16*>(tile_at(cslot, c, r)) = h;
+                            if (r < c)
+                                *reinterpret_cast<bf16*>(tile_at(rslot, r, c)) = h;
+                        }
+                    }
+                }
+            }
+    }
+    NS_WAIT_LDS_BARRIER();
+    // block (bj, bi): global row gbj + c, columns gbi ..
+    tile_store(ws, out + gbj * ld + gbi, ld, wave, lane);
+    if (diag)
+        return;
+
+    // this lane's bf16(v) back from the tile (rows r0..r0+3 of column c)
+    uint2 hv[4][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+                hv[i][j][rg] = *reinterpret_cast<const uint2*>(
+                    tile_at(j < 2 ? cs0 : cs1, wc * 128 + j * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
+    // pass 2 overwrites the tile: every wavefront's copy and reads are done
+    NS_WAIT_LDS_BARRIER();
+    // Branch-free lane roles: an even lane keeps rows r0, r0+1 (d.x) and
+    // writes them at columns c, c+1; an odd lane keeps rows r0+2, r0+3 (d.y)
+    // and writes them at columns c-1, c. v_perm_b32 picks the 16-bit halves
+    // (bytes 0..3 = the kept dword, 4..7 = the received one).
+    const uint32_t odd = fr & 1;
+    const uint32_t keep_y = 0u - odd;
+    const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
+    const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        char* rslot = i < 2 ? rs0 : rs1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c = wc * 128 + j * 32 + fr;
+                const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
+                const uint2 d = hv[i][j][rg];   // x: rows r0, r0+1; y: rows r0+2, r0+3
+                const uint32_t mine = (d.y & keep_y) | (d.x & ~keep_y);
+                const uint32_t send = (d.x & keep_y) | (d.y & ~keep_y);
+                // lane fr ^ 1 (same rows, column c ^ 1)
+                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+                const uint32_t w0 = __builtin_amdgcn_perm(recv, mine, sel0);
+                const uint32_t w1 = __builtin_amdgcn_perm(recv, mine, sel1);
+                const int rr = r0 + 2 * (int)odd;
+                const int cc0 = c - (int)odd;
+                *reinterpret_cast<uint32_t*>(tile_at(rslot, rr, cc0)) = w0;
+                *reinterpret_cast<uint32_t*>(tile_at(rslot, rr + 1, cc0)) = w1;
+            }
+    }
+    NS_WAIT_LDS_BARRIER();
+    // block (bi, bj): global row gbi + r, columns gbj ..
+    tile_store(ws, out + gbi * ld + gbj, ld, wave, lane);
+}
+
 template <int DT, int STAGE, int LAST>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
                                                       const Tile* __restrict__ tiles, int cur,
@@ -754,6 +934,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     __shared__ __attribute__((aligned(1024))) char sl1[2 * kSlotOpBytes];
     __shared__ __attribute__((aligned(1024))) char sl2[2 * kSlotOpBytes];
     __shared__ __attribute__((aligned(1024))) char sl3[2 * kSlotOpBytes];
+    // bf16 update and bA + cA^2 only: quarter 3 of the epilogue's block,
+    // loaded before the K loop so that the epilogue need not wait for it
+    // (160 KB of LDS in all)
+    __shared__ __attribute__((aligned(1024))) char lo3[2 * kSlotOpBytes];
 
     const Tile t = tiles[blockIdx.x];
     const LargeMat& M = mats[t.mat];
@@ -821,6 +1005,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // zeros without memory traffic. (voffset < 2^29 and ranges < 2^31, so the
     // 32-bit offset sum cannot wrap back into range.)
     constexpr bool kIdent = STAGE == 2 && IsBf16<OpT>::value;
+    // epilogue block preloaded into LDS: X_lo (bf16 update), A (bf16 bA + cA^2)
+    constexpr bool kPre = kIdent || (STAGE == 1 && IsBf16<OpT>::value);
     const int sb = kIdent ? t.bi * 8 : 0;
     const int soff_end = range_p > range_q ? range_p : range_q;
     auto issue = [&](char* sp, int s, int q0 = 0, int q1 = 4) __attribute__((always_inline)) {
@@ -961,12 +1147,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         }
     };
 
-    // The bf16 update's epilogue reads the tile's X_lo through LDS (row c =
-    // tile column c, 64 rows per slot). The last three steps have no operand
-    // slot left to load; they load quarters 0..2 of that X_lo tile into the
-    // ring positions they free instead (8 loads per wavefront, like a slot).
+    // The bf16 update's epilogue reads the tile's X_lo through LDS, and the
+    // bf16 bA + cA^2 epilogue the mirrored block of A (row c = tile column c,
+    // 64 rows per slot). The last three steps have no operand slot left to
+    // load; they load quarters 0..2 of that block into the ring positions
+    // they free instead (8 loads per wavefront, like a slot). Quarter 3 goes
+    // to a fifth slot before the K loop.
+    const bf16* pre_blk = nullptr;
+    if constexpr (kPre)
+        pre_blk = static_cast<const bf16*>(kIdent ? M.xlo : M.a) + gbj * M.ldt + gbi;
     auto issue_lo = [&](char* sp, int quarter, int q0, int q1) __attribute__((always_inline)) {
-        issue_lo_quarter(M, gbi, gbj, sp, quarter, wave, lane, q0, q1);
+        issue_blk_quarter(pre_blk, M.ldt, sp, quarter, wave, lane, q0, q1);
     };
 
     uint4 fa[4], fb[4], ga[4], gb[4];
@@ -1002,9 +1193,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         step(sl3, sl2, sl0, s + 3, p3, Peel<-1>{});
     };
     // the last four steps (s = ns - 4); the refills of slots ns .. ns + 2
-    // are the X_lo quarters in the bf16 update, dummy reloads otherwise
+    // are the epilogue block's quarters where there is one, dummy reloads
+    // otherwise
     auto ring_last = [&](int s, auto p0, auto p1, auto p2, auto p3) __attribute__((always_inline)) {
-        if constexpr (kIdent) {
+        if constexpr (kPre) {
             step(sl0, sl3, sl1, s, p0, Peel<-1>{});
             step(sl1, sl0, sl2, s + 1, p1, Peel<0>{});
             step(sl2, sl1, sl3, s + 2, p2, Peel<1>{});
@@ -1014,6 +1206,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         }
     };
 
+    // (the epilogue block's quarter 3 first: the oldest loads, so the wait
+    // counts below, which only bound the number of younger loads, still hold)
+    if constexpr (kPre)
+        issue_blk_quarter(pre_blk, M.ldt, lo3, 3, wave, lane);
     issue(sl0, 0);
     issue(sl1, 1);
     issue(sl2, 2);
@@ -1023,7 +1219,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // operand block read the same k-slice at about the same time (L2 reuse);
     // the bf16 update's identity slots are peeled in place.
     int s = 0;
-    bool lo_pre = false;   // X_lo quarters 0..2 already in slots 0..2
+    bool lo_pre = false;   // epilogue block quarters 0..2 already in slots 0..2
     if constexpr (kIdent) {
         for (; s < sb; s += 4)
             ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
@@ -1038,6 +1234,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             ring_last(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
             lo_pre = true;
         }
+    } else if constexpr (kPre) {
+        // (ns >= 8 and a multiple of 4)
+        for (; s + 4 < ns; s += 4)
+            ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
+        ring_last(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
+        lo_pre = true;
     } else {
         for (; s < ns; s += 4)
             ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
@@ -1046,6 +1248,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
 
     // Epilogues. Lane l, block (i, j), register group rg holds rows
     // lr0..lr0+3 of column lc (tile-local).
+    if constexpr (STAGE == 0 && IsBf16<OpT>::value) {
+        sym_epilogue_bf16<0>(M, sl0, sl1, sl2, sl3, acc, gbi, gbj, t.bi == t.bj, cb, cc, wave, lane);
+        return;
+    } else if constexpr (STAGE == 1 && IsBf16<OpT>::value) {
+        sym_epilogue_bf16<1>(M, sl0, sl1, sl2, lo3, acc, gbi, gbj, t.bi == t.bj, cb, cc, wave, lane);
+        return;
+    }
     if (STAGE == 0 || STAGE == 1) {
         const int64_t ld = M.ldt;
         OpT* out = static_cast<OpT*>(STAGE == 0 ? M.a : M.b);
@@ -1159,7 +1368,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         const int nxt = cur ^ 1;
         const int64_t ldx = M.ldx, ldt = M.ldt;
         if constexpr (kIdent) {
-            update_epilogue_bf16<LAST != 0>(M, sl0, sl1, sl2, sl3, lo_pre, acc, gbi, gbj, nxt, ca, wave, lane);
+            update_epilogue_bf16<LAST != 0>(M, sl0, sl1, sl2, lo3, lo_pre, acc, gbi, gbj, nxt, ca, wave, lane);
             return;
         }
         // The part of aX not yet in the accumulators, per lane four rows of a
