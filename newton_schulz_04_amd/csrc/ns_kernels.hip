@@ -641,7 +641,9 @@ __device__ __forceinline__ void issue_blk_quarter(const bf16* blk, int64_t ld, c
 // Epilogue of the bf16 update (X^T layout, LDS tile row = tile column c):
 //   X_lo tile -> LDS (quarter 3 in its own slot, loaded before the K loop;
 //   quarters 0..2 by the K loop's last steps), y = acc + a X_lo,
-//   LDS <- bf16(y), X_lo <- bf16(y - bf16(y)) (global, in place, from registers)
+//   LDS <- bf16(y), X_lo <- bf16(y - bf16(y)) (global, in place, from
+//   registers: lanes l and l + 32 trade register groups so that each holds 8
+//   consecutive rows of its column, one 16-byte store)
 //   LDS -> X_hi (next slot)
 // Every element is read and rewritten by the same lane in the accumulator
 // passes, so only the copies need barriers. On the last step bf16(y) goes to
@@ -690,7 +692,8 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                 los[j][rg] = *reinterpret_cast<const bf16x4*>(
                     tile_at(j < 2 ? cs0 : cs1, wc * 128 + j * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            uint2 l2[4];   // new X_lo of rows r0..r0+3, register groups 0..3
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int c = wc * 128 + j * 32 + fr;
@@ -704,13 +707,9 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                     hi[e] = (bf16)y;
                     lo2[e] = (bf16)(y - (float)hi[e]);
                 }
+                l2[rg] = __builtin_bit_cast(uint2, lo2);
                 if (staged) {
                     *a = hi;
-                    // the new X_lo goes straight to this tile's own X_lo block
-                    // (its loads have landed); L2 merges the 16-byte pieces of
-                    // each column into whole lines
-                    if (!LAST)
-                        *reinterpret_cast<bf16x4*>(lo_g + (int64_t)c * ldt + r0) = lo2;
                 } else {
                     // last step, rows <= cols: the caller's buffer is X itself
                     const int64_t gr = gbi + r0, gc = gbj + c;
@@ -722,6 +721,24 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                     }
                 }
             }
+            if (!LAST) {
+                // Lane fr holds rows 8 rg + (0..3) of the block row, lane
+                // fr + 32 rows 8 rg + (4..7). Swapping group 2h + 1 of the
+                // lower lane with group 2h of the upper one leaves the lower
+                // lane rows 16h + (0..7) and the upper one rows 16h + (8..15).
+                // The new X_lo goes straight to this tile's own X_lo block
+                // (its loads have landed).
+                const int c = wc * 128 + j * 32 + fr;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const auto sx = __builtin_amdgcn_permlane32_swap(l2[2 * h].x, l2[2 * h + 1].x, false, false);
+                    const auto sy = __builtin_amdgcn_permlane32_swap(l2[2 * h].y, l2[2 * h + 1].y, false, false);
+                    const uint4 v = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                    const int r = wr * 128 + i * 32 + 16 * h + 8 * fg;
+                    *reinterpret_cast<uint4*>(lo_g + (int64_t)c * ldt + r) = v;
+                }
+            }
+        }
     }
     if (!staged)
         return;
