@@ -604,6 +604,75 @@ __device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld
     }
 }
 
+// Whole-tile copy into the caller's matrix (the last step): tile row R goes
+// to row row0 + R of the caller's buffer (rows of `cols` elements, or the row
+// table), elements col0 .. col0 + 255; rows >= nrows and elements >= ncols
+// (the padding) are not written. Same lane mapping as tile_store.
+__device__ __forceinline__ void tile_store_user(const char* ws, bf16* user, void* const* rows_tab, int64_t cols,
+                                                int64_t row0, int64_t nrows, int64_t col0, int64_t ncols,
+                                                int wave, int lane)
+{
+    const int half = lane >> 5, p = lane & 31;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+        const int R = wave * 64 + 2 * q + half;
+        const int64_t row = row0 + R, c0 = col0 + 8 * (p ^ (R & 31));
+        const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
+        if (row < nrows) {
+            bf16* dst = grow<bf16>(user, rows_tab, cols, row) + c0;
+            if (c0 + 8 <= ncols && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+                const bf16x8 h = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (c0 + e < ncols)
+                        dst[e] = h[e];
+            }
+        }
+    }
+}
+
+// Writes a 256 x 256 bf16 tile held in the accumulator order (hv[i][j][rg]:
+// rows r0 .. r0 + 3 of column c, r0 = 128 wr + 32 i + 8 rg + 4 fg,
+// c = 128 wc + 32 j + fr) into the LDS tile with LDS row = tile row (slot
+// r >> 6 = 2 wr + (i >> 1): rs0 for i < 2, rs1 otherwise). Lanes fr and
+// fr ^ 1 hold adjacent columns of the same four rows; one exchange of a dword
+// gives each of them two rows of a column pair, written as 4-byte pieces:
+// an even lane keeps rows r0, r0+1 (d.x) for columns c, c+1, an odd lane
+// rows r0+2, r0+3 (d.y) for columns c-1, c. v_perm_b32 picks the 16-bit
+// halves (bytes 0..3 = the kept dword, 4..7 = the received one).
+__device__ __forceinline__ void write_tile_by_rows(char* rs0, char* rs1, const uint2 (&hv)[4][4][4], int wr,
+                                                   int wc, int fr, int fg)
+{
+    const uint32_t odd = fr & 1;
+    const uint32_t keep_y = 0u - odd;
+    const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
+    const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        char* rslot = i < 2 ? rs0 : rs1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c = wc * 128 + j * 32 + fr;
+                const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
+                const uint2 d = hv[i][j][rg];   // x: rows r0, r0+1; y: rows r0+2, r0+3
+                const uint32_t mine = (d.y & keep_y) | (d.x & ~keep_y);
+                const uint32_t send = (d.x & keep_y) | (d.y & ~keep_y);
+                // lane fr ^ 1 (same rows, column c ^ 1)
+                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+                const uint32_t w0 = __builtin_amdgcn_perm(recv, mine, sel0);
+                const uint32_t w1 = __builtin_amdgcn_perm(recv, mine, sel1);
+                const int rr = r0 + 2 * (int)odd;
+                const int cc0 = c - (int)odd;
+                *reinterpret_cast<uint32_t*>(tile_at(rslot, rr, cc0)) = w0;
+                *reinterpret_cast<uint32_t*>(tile_at(rslot, rr + 1, cc0)) = w1;
+            }
+    }
+}
+
 #define NS_WAIT_ALL_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 #define NS_WAIT_DMA_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory")
 #define NS_WAIT_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
@@ -677,8 +746,11 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
         NS_WAIT_DMA_BARRIER();
     }
 
-    const bool staged = !LAST || M.trans;
+    // last step, rows <= cols: the caller's buffer is X itself, so the tile
+    // is restaged with LDS row = tile row
+    const bool by_rows = LAST && !M.trans;
     bf16* user = static_cast<bf16*>(M.user);
+    uint2 hv[4][4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         // The 16 reads of a block row go out together: the writes below could
@@ -708,18 +780,10 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                     lo2[e] = (bf16)(y - (float)hi[e]);
                 }
                 l2[rg] = __builtin_bit_cast(uint2, lo2);
-                if (staged) {
+                if (LAST && by_rows)
+                    hv[i][j][rg] = __builtin_bit_cast(uint2, hi);
+                else
                     *a = hi;
-                } else {
-                    // last step, rows <= cols: the caller's buffer is X itself
-                    const int64_t gr = gbi + r0, gc = gbj + c;
-                    if (gc < M.n) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (gr + e < M.m)
-                                grow<bf16>(user, M.rows_tab, M.cols, gr + e)[gc] = hi[e];
-                    }
-                }
             }
             if (!LAST) {
                 // Lane fr holds rows 8 rg + (0..3) of the block row, lane
@@ -740,30 +804,16 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
             }
         }
     }
-    if (!staged)
-        return;
-
     NS_WAIT_LDS_BARRIER();
     if (LAST) {
-        // last step, rows > cols: the caller's buffer is X^T, rows of M.cols
-        const int half = lane >> 5, p = lane & 31;
-#pragma unroll 4
-        for (int q = 0; q < 32; ++q) {
-            const int R = wave * 64 + 2 * q + half;
-            const int64_t c = gbj + R, r0 = gbi + 8 * (p ^ (R & 31));
-            const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
-            if (c < M.n) {
-                bf16* dst = grow<bf16>(user, M.rows_tab, M.cols, c) + r0;
-                if (r0 + 8 <= M.m && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                    *reinterpret_cast<uint4*>(dst) = v;
-                } else {
-                    const bf16x8 h = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (r0 + e < M.m)
-                            dst[e] = h[e];
-                }
-            }
+        if (by_rows) {
+            // (the barrier above: every wavefront has read its X_lo)
+            write_tile_by_rows(wr ? sl2 : sl0, wr ? sl3 : sl1, hv, wr, wc, fr, fg);
+            NS_WAIT_LDS_BARRIER();
+            tile_store_user(ws, user, M.rows_tab, M.cols, gbi, M.m, gbj, M.n, wave, lane);
+        } else {
+            // rows > cols: the caller's buffer is X^T, rows of M.cols
+            tile_store_user(ws, user, M.rows_tab, M.cols, gbj, M.n, gbi, M.m, wave, lane);
         }
         return;
     }
@@ -777,9 +827,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
 //   1. LDS row = tile column c (the accumulator order, 8 bytes per lane and
 //      register group; for STAGE 1 the same places hold the block of A read
 //      by the K loop's last steps, A[c][r] = A[r][c]) -> block (bj, bi).
-//   2. LDS row = tile row r -> block (bi, bj). Lanes fr and fr ^ 1 hold
-//      adjacent columns of the same four rows; one exchange of a dword gives
-//      each of them two rows of a column pair, written as 4-byte pieces.
+//   2. LDS row = tile row r -> block (bi, bj) (write_tile_by_rows).
 // On a diagonal tile only the upper triangle is used: pass 1 writes each
 // upper element at both (c, r) and (r, c), so the block is exactly symmetric,
 // and pass 2 is not needed. The diagonal keeps its bf16 rounding residue
@@ -902,36 +950,7 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
                     tile_at(j < 2 ? cs0 : cs1, wc * 128 + j * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
     // pass 2 overwrites the tile: every wavefront's copy and reads are done
     NS_WAIT_LDS_BARRIER();
-    // Branch-free lane roles: an even lane keeps rows r0, r0+1 (d.x) and
-    // writes them at columns c, c+1; an odd lane keeps rows r0+2, r0+3 (d.y)
-    // and writes them at columns c-1, c. v_perm_b32 picks the 16-bit halves
-    // (bytes 0..3 = the kept dword, 4..7 = the received one).
-    const uint32_t odd = fr & 1;
-    const uint32_t keep_y = 0u - odd;
-    const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
-    const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        char* rslot = i < 2 ? rs0 : rs1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int c = wc * 128 + j * 32 + fr;
-                const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
-                const uint2 d = hv[i][j][rg];   // x: rows r0, r0+1; y: rows r0+2, r0+3
-                const uint32_t mine = (d.y & keep_y) | (d.x & ~keep_y);
-                const uint32_t send = (d.x & keep_y) | (d.y & ~keep_y);
-                // lane fr ^ 1 (same rows, column c ^ 1)
-                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-                const uint32_t w0 = __builtin_amdgcn_perm(recv, mine, sel0);
-                const uint32_t w1 = __builtin_amdgcn_perm(recv, mine, sel1);
-                const int rr = r0 + 2 * (int)odd;
-                const int cc0 = c - (int)odd;
-                *reinterpret_cast<uint32_t*>(tile_at(rslot, rr, cc0)) = w0;
-                *reinterpret_cast<uint32_t*>(tile_at(rslot, rr + 1, cc0)) = w1;
-            }
-    }
+    write_tile_by_rows(rs0, rs1, hv, wr, wc, fr, fg);
     NS_WAIT_LDS_BARRIER();
     // block (bi, bj): global row gbi + r, columns gbj ..
     tile_store(ws, out + gbi * ld + gbj, ld, wave, lane);
