@@ -979,9 +979,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     const LargeMat& M = mats[t.mat];
     const char* P;
     const char* Q;
-    constexpr bool kTrans = STAGE == 0 && IsBf16<OpT>::value;
+    // Operands read as k-rows (32 rows of 512 bytes per slot, see above)
+    // instead of the tile's rows (256 rows of 64 bytes): on the bf16 path X^T
+    // for X X^T, and A, B, which are symmetric, so that their k-rows restricted
+    // to a block's columns are that block's rows. The update's X^T operand has
+    // k contiguous in its rows. Long row pieces move faster: a 1 KB DMA covers
+    // 2 rows of 512 bytes instead of 16 of 64.
+    constexpr bool kTP = IsBf16<OpT>::value;
+    constexpr bool kTQ = IsBf16<OpT>::value && STAGE != 2;
     int64_t K, pitch;
-    if (kTrans) {
+    if (STAGE == 0 && IsBf16<OpT>::value) {
         P = Q = static_cast<const char*>(M.xt[cur]);
         K = M.np;
         pitch = M.ldt;
@@ -1012,12 +1019,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // Buffer resources over the 256-row blocks of P and Q (out-of-range reads
     // return 0 without touching memory; only the K loop's loads past the last
     // slot use that, see issue()).
-    // (Transposed operands: the blocks are column ranges of X^T and the
-    // resource spans all np rows.)
-    const int64_t poff = kTrans ? (int64_t)t.bi * kTile * 2 : (int64_t)t.bi * kTile * ldb;
-    const int64_t qoff = kTrans ? (int64_t)t.bj * kTile * 2 : (int64_t)t.bj * kTile * ldb;
-    const int range_p = kTrans ? (int)((int64_t)M.np * ldb - poff) : kTile * ldb;
-    const int range_q = kTrans ? (int)((int64_t)M.np * ldb - qoff) : kTile * ldb;
+    // (k-row operands: the blocks are column ranges and the resource spans
+    // all K rows.)
+    const int64_t poff = kTP ? (int64_t)t.bi * kTile * 2 : (int64_t)t.bi * kTile * ldb;
+    const int64_t qoff = kTQ ? (int64_t)t.bj * kTile * 2 : (int64_t)t.bj * kTile * ldb;
+    const int range_p = kTP ? (int)(K * ldb - poff) : kTile * ldb;
+    const int range_q = kTQ ? (int)(K * ldb - qoff) : kTile * ldb;
     const __amdgpu_buffer_rsrc_t rp =
         __builtin_amdgcn_make_buffer_rsrc((void*)(P + poff), (short)0, range_p, 0x00020000);
     const __amdgpu_buffer_rsrc_t rq =
@@ -1027,12 +1034,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // slot operand, 1 KB = rows 16I..16I+15 each. Lane l writes stored chunk
     // l & 3 of row 16I + (l >> 2), i.e. logical chunk (l & 3) ^ g(row); the
     // q offset (64 rows) leaves g unchanged.
-    // Transposed: instruction I fills LDS rows 2I, 2I+1 (k); lane l writes
+    // k-rows: instruction I fills LDS rows 2I, 2I+1 (k); lane l writes
     // stored chunk l & 31 of row 2I + (l >> 5); the q offset (8 rows) leaves
     // the swizzle unchanged.
-    const int dma_row = kTrans ? 2 * wave + (lane >> 5) : 16 * wave + (lane >> 2);
-    const int dma_voff = kTrans ? dma_row * ldb + (((lane & 31) ^ tr_swz(dma_row)) << 4)
-                                : dma_row * ldb + (((lane & 3) ^ lds_swz(dma_row)) << 4);
+    const int row_n = 16 * wave + (lane >> 2), row_t = 2 * wave + (lane >> 5);
+    const int voff_n = row_n * ldb + (((lane & 3) ^ lds_swz(row_n)) << 4);
+    const int voff_t = row_t * ldb + (((lane & 31) ^ tr_swz(row_t)) << 4);
+    const int voff_p = kTP ? voff_t : voff_n;
+    const int voff_q = kTQ ? voff_t : voff_n;
 
     // In the bf16 update, slots sb .. sb + 7 are this tile's own 256 rows.
     // Slot positions past the end (s >= ns) are loads that nobody reads but
@@ -1048,12 +1057,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     auto issue = [&](char* sp, int s, int q0 = 0, int q1 = 4) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = q0; q < q1; ++q) {
-            const int soff = s >= ns ? soff_end
-                                     : kTrans ? (s * 32 + 8 * q) * ldb : s * kSlotRowBytes + q * 64 * ldb;
+            const int soff_t = s >= ns ? soff_end : (s * 32 + 8 * q) * ldb;
+            const int soff_n = s >= ns ? soff_end : s * kSlotRowBytes + q * 64 * ldb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
+                rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, voff_p, kTP ? soff_t : soff_n, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rq, (lds_ptr_t)(sp + kSlotOpBytes + (wave + 4 * q) * 1024), 16, dma_voff, soff, 0, 0);
+                rq, (lds_ptr_t)(sp + kSlotOpBytes + (wave + 4 * q) * 1024), 16, voff_q, kTQ ? soff_t : soff_n, 0, 0);
         }
     };
 
@@ -1070,38 +1079,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
 
     // Fragment offsets (k-step 0) of this lane's rows inside a stage; k-step
     // ks is logical chunk 2 ks + fg, which XORs the stored chunk with 2 ks.
-    // Transposed: lane l (group g = l >> 4, x = l & 15) reads row
+    // k-rows: lane l (group g = l >> 4, x = l & 15) reads row
     // ks*16 + 8 (g >> 1) + 4 e + (x >> 2), columns base + 16 (g & 1) + 4 (x & 3);
     // k-step ks and half e only add whole rows (ks * 8192 + e * 2048 bytes).
+    // Both layouts give lane l the k values 16 ks + 8 (l >> 5) + 0..7 of its
+    // row or column, so they can be mixed.
+    auto off_t = [&](int base) {
+        const int g = lane >> 4, x = lane & 15;
+        const int kr = 8 * (g >> 1) + (x >> 2);
+        const int cl = base + 16 * (g & 1) + 4 * (x & 3);
+        return kr * kTrRowBytes + (((cl >> 3) ^ tr_swz(kr)) << 4) + (cl & 7) * 2;
+    };
     int aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (kTrans) {
-            const int g = lane >> 4, x = lane & 15;
-            const int kr = 8 * (g >> 1) + (x >> 2);
-            const int ca = wr * 128 + i * 32 + 16 * (g & 1) + 4 * (x & 3);
-            const int cb = wc * 128 + i * 32 + 16 * (g & 1) + 4 * (x & 3);
-            aoff[i] = kr * kTrRowBytes + (((ca >> 3) ^ tr_swz(kr)) << 4) + (ca & 7) * 2;
-            boff[i] = kSlotOpBytes + kr * kTrRowBytes + (((cb >> 3) ^ tr_swz(kr)) << 4) + (cb & 7) * 2;
-        } else {
-            aoff[i] = lds_off(wr * 128 + i * 32 + fr, fg);
-            boff[i] = kSlotOpBytes + lds_off(wc * 128 + i * 32 + fr, fg);
-        }
+        aoff[i] = kTP ? off_t(wr * 128 + i * 32) : lds_off(wr * 128 + i * 32 + fr, fg);
+        boff[i] = kSlotOpBytes + (kTQ ? off_t(wc * 128 + i * 32) : lds_off(wc * 128 + i * 32 + fr, fg));
     }
+    auto read_frag = [&](const char* sp, int off, int ks, bool tr) __attribute__((always_inline)) {
+        if (tr) {
+            const uint2 v0 = ds_read_tr(sp + off + ks * 8192);
+            const uint2 v1 = ds_read_tr(sp + off + ks * 8192 + 2048);
+            return make_uint4(v0.x, v0.y, v1.x, v1.y);
+        }
+        return *reinterpret_cast<const uint4*>(sp + (off ^ (ks << 5)));
+    };
     auto read_frags = [&](const char* sp, int ks, uint4 (&af)[4], uint4 (&bfr)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (kTrans) {
-                const uint2 a0 = ds_read_tr(sp + aoff[i] + ks * 8192);
-                const uint2 a1 = ds_read_tr(sp + aoff[i] + ks * 8192 + 2048);
-                const uint2 b0 = ds_read_tr(sp + boff[i] + ks * 8192);
-                const uint2 b1 = ds_read_tr(sp + boff[i] + ks * 8192 + 2048);
-                af[i] = make_uint4(a0.x, a0.y, a1.x, a1.y);
-                bfr[i] = make_uint4(b0.x, b0.y, b1.x, b1.y);
-            } else {
-                af[i] = *reinterpret_cast<const uint4*>(sp + (aoff[i] ^ (ks << 5)));
-                bfr[i] = *reinterpret_cast<const uint4*>(sp + (boff[i] ^ (ks << 5)));
-            }
+            af[i] = read_frag(sp, aoff[i], ks, kTP);
+            bfr[i] = read_frag(sp, boff[i], ks, kTQ);
         }
     };
     auto mfma_block = [&](const uint4 (&af)[4], const uint4 (&bfr)[4]) {
@@ -1113,11 +1120,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     };
     auto interleave = []() __attribute__((always_inline)) {
         // Per k-step: the 16 MFMAs with the LDS reads of the next k-step
-        // (16 transposed 8-byte reads or 8 16-byte reads) and half of the
-        // refill's DMAs (4) spread between them. Issued in one burst, the
-        // DMAs stall the wavefront at issue while the memory pipeline is
+        // (8 transposed 8-byte reads or 4 16-byte reads per operand) and half
+        // of the refill's DMAs (4) spread between them. Issued in one burst,
+        // the DMAs stall the wavefront at issue while the memory pipeline is
         // full, and that pipeline then runs dry during the MFMAs.
-        constexpr int nreads = kTrans ? 16 : 8;
+        constexpr int nreads = (kTP ? 8 : 4) + (kTQ ? 8 : 4);
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             if (q % 4 == 0)
