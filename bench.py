@@ -53,7 +53,7 @@ def make_workload(name):
     return mats, desc
 
 
-def cpu_baseline(sample_rows=4096, sample_cols=3072):
+def cpu_baseline(sample_rows=6144, sample_cols=4608):
     """The fp64 oracle, as it stands, on a bounded sample of the workload: one
     Newton-Schulz step on the top-left sample_rows x sample_cols block of
     matrix 0. Scaled to matrices/s by metric FLOPs (an optimistic scaling for

@@ -4,9 +4,15 @@ profiles/ (host-side parsing only; nothing here touches the GPU).
     python -m newton_schulz_04_amd.profiling stats KERNEL_STATS_CSV OUT_MD --command "..."
     python -m newton_schulz_04_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_JSON --command "..."
     python -m newton_schulz_04_amd.profiling summary KERNEL_STATS_CSV TRAFFIC_JSON BENCH_JSON OUT_MD --title ... --command "..."
+        [--mfma-csv MFMA_COUNTERS_CSV --mfma-command "..."]
 
 `stats` reads the kernel statistics that `rocprofv3 --kernel-trace --stats`
 writes and tabulates the per-kernel average durations.
+
+The optional MFMA counter run (`rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE`) gives each GEMM's MFMA utilisation (busy
+cycles of the 4 matrix units per compute unit over the compute units' busy
+cycles) and its average shader clock (GRBM_GUI_ACTIVE counts per XCD).
 
 `traffic` reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
 `bench.py --copy-probe` (counter values in KiB per dispatch). The copy probe
@@ -28,6 +34,8 @@ COPY_PROBE_BYTES = 1 << 30
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # GEMM stage template argument -> the name bench.py reports it under
 GEMM_KINDS = {"0": "syrk", "1": "poly", "2": "update"}
+XCDS = 8
+SIMDS_PER_CU = 4
 
 
 def source_hash():
@@ -137,21 +145,69 @@ def algorithmic_bytes(shapes, elt=2):
     return out
 
 
-def summary_md(stats_csv, traffic_json, bench_json, title, shapes, kt_command):
+def mfma_table(mfma_csv):
+    """Per GEMM kind: MFMA utilisation and shader clock, averaged over its
+    dispatches in the counter run."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    span = {}
+    with open(mfma_csv) as f:
+        for row in csv.DictReader(f):
+            kind = kernel_kind(row["Kernel_Name"])
+            if kind not in ("syrk", "poly", "update"):
+                continue
+            key = (kind, row["Dispatch_Id"])
+            acc[key][row["Counter_Name"]].append(float(row["Counter_Value"]))
+            span[key] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
+    per_kind = collections.defaultdict(list)
+    for (kind, _), c in acc.items():
+        busy = sum(c["SQ_BUSY_CU_CYCLES"])
+        mfma = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"])
+        grbm = sum(c["GRBM_GUI_ACTIVE"])
+        if busy <= 0 or span[(kind, _)] <= 0:
+            continue
+        per_kind[kind].append((mfma / (SIMDS_PER_CU * busy), grbm / XCDS / span[(kind, _)] / 1e9))
+    rows = ["| kernel | dispatches | MFMA busy | shader clock (GHz) |", "|---|---|---|---|"]
+    for kind in ("syrk", "poly", "update"):
+        v = per_kind.get(kind)
+        if v:
+            u = sum(x[0] for x in v) / len(v)
+            g = sum(x[1] for x in v) / len(v)
+            rows.append(f"| {kind} | {len(v)} | {100 * u:.1f}% | {g:.2f} |")
+    return "\n".join(rows)
+
+
+def summary_md(stats_csv, traffic_json, bench_json, title, shapes, kt_command, mfma_csv=None, mfma_command=None):
     with open(traffic_json) as f:
         t = json.load(f)
     with open(bench_json) as f:
         b = json.loads(f.read().strip().splitlines()[-1])
     alg = algorithmic_bytes(shapes)
     ks = {k: v["ms_avg"] for k, v in b["kernels"].items()}
-    rows = ["| kernel | fetch (GB/launch) | write (GB/launch) | algorithmic read / write (GB) |",
-            "|---|---|---|---|"]
+    rows = ["| kernel | fetch (GB/launch) | write (GB/launch) | algorithmic read / write (GB) | fetch + write per launch time |",
+            "|---|---|---|---|---|"]
     for k in ("update", "syrk", "poly", "prep", "norm_partial"):
         e = t["kernels"].get(k)
         if not e:
             continue
+        rate = ""
+        if ks.get(k):
+            rate = f"{(e['fetch_bytes'] + e['write_bytes']) / (ks[k] * 1e-3) / 1e12:.2f} TB/s"
         rows.append(f"| {k} | {e['fetch_bytes'] / 1e9:.2f} | {e['write_bytes'] / 1e9:.2f} | "
-                    f"{alg[k + ' read'] / 1e9:.2f} / {alg[k + ' write'] / 1e9:.2f} |")
+                    f"{alg[k + ' read'] / 1e9:.2f} / {alg[k + ' write'] / 1e9:.2f} | {rate} |")
+    mfma = ""
+    if mfma_csv:
+        mfma = f"""
+## MFMA utilisation (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE)
+
+    {mfma_command}
+
+{mfma_table(mfma_csv)}
+
+The bf16 MFMA peak assumes 2.4 GHz; the shader clock under this load is what
+the power limit leaves. syrk and poly compute only the upper-triangle tiles
+(300 of 576 per 6144 x 6144 output), so their metric TFLOP/s count about
+twice the MFMA work they do.
+"""
     cp = t["copy_probe"]
     return f"""# {title}
 
@@ -184,8 +240,8 @@ caller's buffer instead of X_hi and X_lo):
 
 The record with a hash of the library sources is `{os.path.basename(traffic_json)}`;
 bench.py reports the dominant kernel's bytes as `roofline.traffic` only while
-the hash matches.
-"""
+the hash matches. prep and norm_partial are the HBM-bound passes (peak 8 TB/s).
+{mfma}"""
 
 
 def main():
@@ -200,6 +256,8 @@ def main():
     m.add_argument("--shape", default="8192x6144")
     m.add_argument("--count", type=int, default=8)
     m.add_argument("--command", required=True)
+    m.add_argument("--mfma-csv")
+    m.add_argument("--mfma-command")
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("out")
@@ -214,7 +272,7 @@ def main():
         r, c = (int(v) for v in a.shape.split("x"))
         with open(a.out, "w") as f:
             f.write(summary_md(a.stats_csv, a.traffic_json, a.bench_json, a.title, [(r, c)] * a.count,
-                               a.command))
+                               a.command, a.mfma_csv, a.mfma_command))
     elif a.what == "stats":
         with open(a.out, "w") as f:
             f.write(stats_md(a.csv, a.command))
