@@ -379,7 +379,6 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
     const int64_t i0 = (int64_t)(local / per_row) * kPrepTile;
     const int64_t j0 = (int64_t)(local % per_row) * kPrepTile;
     const float s = inv[mi];
-    const T* g = static_cast<const T*>(M.user);
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     if constexpr (DT == 0) {
         if (M.trans) {
@@ -1298,36 +1297,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         sym_epilogue_bf16<1>(M, sl0, sl1, sl2, lo3, acc, gbi, gbj, t.bi == t.bj, cb, cc, wave, lane);
         return;
     }
+    // fp32 path: the epilogues store straight from the accumulators (a
+    // 256 x 256 fp32 tile does not fit the LDS), and there are no residues.
     if (STAGE == 0 || STAGE == 1) {
         const int64_t ld = M.ldt;
         OpT* out = static_cast<OpT*>(STAGE == 0 ? M.a : M.b);
         const OpT* ain = static_cast<const OpT*>(M.a);
         const bool diag = t.bi == t.bj;
-        // bf16: the diagonals of A and B also keep what their bf16 rounding
-        // drops (d_i = v_ii - bf16(v_ii)). With A = A_bf16 + diag(dA), the
-        // first-order B is bA_bf16 + c A_bf16^2 + b diag(dA)
-        // + c A_bf16,ij (dA_i + dA_j); the update adds B's own residue.
-        constexpr bool kDiag = IsBf16<OpT>::value;
-        float* dout = STAGE == 0 ? M.adiag : M.bdiag;
-        float dcol[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (kDiag && STAGE == 1) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dcol[j] = M.adiag[gbj + wc * 128 + j * 32 + fr];
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             // bA + cA^2 needs A at the same places; A is exactly symmetric, so
             // rows r0..r0+3 of column c are A[c][r0..r0+3], one vector load.
             // All 16 loads of a block row are issued before any is used.
             f32x4 a4[4][4];
-            f32x4 drow[4];
-            if constexpr (kDiag && STAGE == 1) {
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg)
-                    drow[rg] = *reinterpret_cast<const f32x4*>(M.adiag + gbi + wr * 128 + i * 32 + rg * 8 +
-                                                              fg * 4);
-            }
             if (STAGE == 1) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -1351,12 +1333,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                         v[e] = acc[i][j][rg * 4 + e];
                     if (STAGE == 1) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float ce = cb;
-                            if constexpr (kDiag)
-                                ce = fmaf(cc, drow[rg][e] + dcol[j], cb);
-                            v[e] = ce * a4[j][rg][e] + cc * v[e];
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = cb * a4[j][rg][e] + cc * v[e];
                     }
                     if (!diag) {
 #pragma unroll
@@ -1389,21 +1367,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                     v = r == sel ? acc[i][i][r] : v;
                 const int64_t rc = gbi + wr * 128 + i * 32 + fr;
                 if (has) {
-                    if (STAGE == 1) {
-                        const float av = to_f32(ain[rc * ld + rc]);
-                        float ce = cb;
-                        if constexpr (kDiag) {
-                            const float da = M.adiag[rc];
-                            ce = fmaf(cc, 2.f * da, cb);
-                            v = fmaf(cb, da, ce * av + cc * v);
-                        } else {
-                            v = ce * av + cc * v;
-                        }
-                    }
-                    const OpT vb = from_f32<OpT>(v);
-                    out[rc * ld + rc] = vb;
-                    if constexpr (kDiag)
-                        dout[rc] = v - to_f32(vb);
+                    if (STAGE == 1)
+                        v = cb * to_f32(ain[rc * ld + rc]) + cc * v;
+                    out[rc * ld + rc] = from_f32<OpT>(v);
                 }
             }
         }
@@ -1414,12 +1380,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             update_epilogue_bf16<LAST != 0>(M, sl0, sl1, sl2, lo3, lo_pre, acc, gbi, gbj, nxt, ca, wave, lane);
             return;
         }
-        // The part of aX not yet in the accumulators, per lane four rows of a
-        // column, stored like X^T: a X_lo on the bf16 path (X_hi was added by
-        // the identity MFMAs), a X on the fp32 path (its operand copy,
-        // read-only in this launch).
-        const OpT* src = static_cast<const OpT*>(kIdent ? M.xlo : M.xt[cur]);
-        OpT* xlo = static_cast<OpT*>(M.xlo);
+        // a X, per lane four rows of a column, from X^T (this launch's
+        // operand copy, read-only here)
+        const OpT* src = static_cast<const OpT*>(M.xt[cur]);
         OpT* xb = static_cast<OpT*>(M.xb[nxt]);
         OpT* xt = static_cast<OpT*>(M.xt[nxt]);
         OpT* user = static_cast<OpT*>(M.user);
@@ -1441,18 +1404,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                               fmaf(ca, x[3], v3)};
                 if (!last) {
                     store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
-                    if (kIdent) {
-                        // new X = X_hi (just stored) + X_lo
-                        float lo[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            lo[e] = y[e] - to_f32(from_f32<OpT>(y[e]));
-                        store4(xlo + c * ldt + r0, lo[0], lo[1], lo[2], lo[3]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
                 } else if (c < M.n) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
