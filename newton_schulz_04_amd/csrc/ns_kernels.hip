@@ -37,6 +37,19 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// bf16 X_hi (the X^T operand of X X^T and of the update) is stored as
+// column panels of 32: X^T element (r, c), r < np, c < mp, sits at
+// ((c >> 5) np + r) 32 + (c & 31). A K slice of 32 of either product is then
+// one panel: the update's 256 rows of it are 16 KB in one piece, and X X^T's
+// 32 k-rows of a 256-column block are 8 pieces of 2 KB, so every 1 KB operand
+// DMA reads one contiguous kilobyte (a row-major X^T gives the update 64-byte
+// pieces, which fetch each 128-byte line twice, once per slot).
+constexpr int kPanelCols = 32;
+__device__ __forceinline__ int64_t pan_at(int64_t np, int64_t r, int64_t c)
+{
+    return ((c >> 5) * np + r) * kPanelCols + (c & 31);
+}
+
 // Element type of a dtype code (0 = bf16, 1 = fp32). Kernels are templated on
 // the code rather than the type so that their names demangle in profilers.
 template <int DT> struct Elt;
@@ -409,7 +422,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
                 h[e >> 3][e & 7] = hb;
                 l[e >> 3][e & 7] = (bf16)(v[e] - (float)hb);
             }
-            bf16* xt = static_cast<bf16*>(M.xt[0]) + j * M.ldt + i;
+            // (i is a multiple of 16: the 16 elements stay in one panel)
+            bf16* xt = static_cast<bf16*>(M.xt[0]) + pan_at(M.np, j, i);
             bf16* xl = static_cast<bf16*>(M.xlo) + j * M.ldt + i;
             *reinterpret_cast<bf16x8*>(xt) = h[0];
             *reinterpret_cast<bf16x8*>(xt + 8) = h[1];
@@ -449,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
                 l[e >> 3][e & 7] = (bf16)(v - (float)hb);
             }
             const int64_t jt = j0 + r, it = i0 + 16 * q;   // X^T row, first element
-            bf16* xt = static_cast<bf16*>(M.xt[0]) + jt * M.ldt + it;
+            bf16* xt = static_cast<bf16*>(M.xt[0]) + pan_at(M.np, jt, it);
             bf16* xl = static_cast<bf16*>(M.xlo) + jt * M.ldt + it;
             *reinterpret_cast<bf16x8*>(xt) = h[0];
             *reinterpret_cast<bf16x8*>(xt + 8) = h[1];
@@ -600,6 +614,26 @@ __device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld
         const int R = wave * 64 + 2 * q + half;
         const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
         *reinterpret_cast<uint4*>(dst + R * ld + 8 * (p ^ (R & 31))) = v;
+    }
+}
+
+// Whole-tile copy from the LDS tile into the panel layout of X_hi: tile row
+// R is X^T row r0 + R, its 256 elements are panels pc0 .. pc0 + 7 (64 bytes
+// each). One instruction writes one panel's 16 consecutive rows, a contiguous
+// kilobyte: lane l = 16 g + 4 a + b takes row 16 rb + g + 4 a, chunk b of
+// panel pp. Within a 16-lane group the stored chunks ((4 pp + b) ^ (R & 31))
+// differ in bits 0-1 (b ^ g) and 2-3 ((pp ^ a) & 3), so the group covers all
+// 64 LDS banks once.
+__device__ __forceinline__ void tile_store_pan(const char* ws, bf16* xt, int64_t np, int64_t r0, int64_t pc0,
+                                               int wave, int lane)
+{
+    const int g = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+        const int rb = q >> 3, pp = q & 7;
+        const int R = wave * 64 + 16 * rb + g + 4 * a;
+        const uint4 v = *reinterpret_cast<const uint4*>(ws + (R & 63) * 512 + (((4 * pp + b) ^ (R & 31)) << 4));
+        *reinterpret_cast<uint4*>(xt + ((pc0 + pp) * np + r0 + R) * kPanelCols + 8 * b) = v;
     }
 }
 
@@ -816,7 +850,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
         }
         return;
     }
-    tile_store(ws, static_cast<bf16*>(M.xt[nxt]) + gbj * ldt + gbi, ldt, wave, lane);
+    tile_store_pan(ws, static_cast<bf16*>(M.xt[nxt]), M.np, gbj, gbi / kPanelCols, wave, lane);
 }
 
 // Epilogue of the bf16 symmetric products A = X X^T (STAGE 0) and
@@ -986,6 +1020,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // 2 rows of 512 bytes instead of 16 of 64.
     constexpr bool kTP = IsBf16<OpT>::value;
     constexpr bool kTQ = IsBf16<OpT>::value && STAGE != 2;
+    // X_hi is stored as column panels (pan_at): X X^T reads its k-rows from
+    // them into an LDS slot laid out as the 8 panels of the block (kPT: 32
+    // rows of 64 bytes each, 2 KB per panel); the update reads its X^T
+    // operand, k contiguous, as usual rows of 64 bytes, from one panel per
+    // slot (kPQ).
+    constexpr bool kPT = IsBf16<OpT>::value && STAGE == 0;
+    constexpr bool kPQ = IsBf16<OpT>::value && STAGE == 2;
     int64_t K, pitch;
     if (STAGE == 0 && IsBf16<OpT>::value) {
         P = Q = static_cast<const char*>(M.xt[cur]);
@@ -1020,10 +1061,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // slot use that, see issue()).
     // (k-row operands: the blocks are column ranges and the resource spans
     // all K rows.)
-    const int64_t poff = kTP ? (int64_t)t.bi * kTile * 2 : (int64_t)t.bi * kTile * ldb;
-    const int64_t qoff = kTQ ? (int64_t)t.bj * kTile * 2 : (int64_t)t.bj * kTile * ldb;
-    const int range_p = kTP ? (int)(K * ldb - poff) : kTile * ldb;
-    const int range_q = kTQ ? (int)(K * ldb - qoff) : kTile * ldb;
+    // (panels: bytes per panel, np rows of 64 bytes; P and Q of X X^T are
+    // the 8 panels of block bi, bj on, the update's Q rows 256 bj on of every
+    // panel)
+    // (all offsets into the panels fit 31 bits: the array is mp np 2 bytes)
+    const int panb = M.np * kSlotRowBytes;
+    const int pan_all = (M.mp / kPanelCols) * panb;
+    const int64_t poff = kPT ? (int64_t)t.bi * 8 * panb
+                       : kTP ? (int64_t)t.bi * kTile * 2 : (int64_t)t.bi * kTile * ldb;
+    const int64_t qoff = kPT ? (int64_t)t.bj * 8 * panb
+                       : kPQ ? (int64_t)t.bj * kTile * kSlotRowBytes
+                       : kTQ ? (int64_t)t.bj * kTile * 2 : (int64_t)t.bj * kTile * ldb;
+    const int range_p = kPT ? (int)(pan_all - poff) : kTP ? (int)(K * ldb - poff) : kTile * ldb;
+    const int range_q = (kPT || kPQ) ? (int)(pan_all - qoff) : kTQ ? (int)(K * ldb - qoff) : kTile * ldb;
     const __amdgpu_buffer_rsrc_t rp =
         __builtin_amdgcn_make_buffer_rsrc((void*)(P + poff), (short)0, range_p, 0x00020000);
     const __amdgpu_buffer_rsrc_t rq =
@@ -1036,11 +1086,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // k-rows: instruction I fills LDS rows 2I, 2I+1 (k); lane l writes
     // stored chunk l & 31 of row 2I + (l >> 5); the q offset (8 rows) leaves
     // the swizzle unchanged.
+    // panel k-rows: instruction I fills panel I >> 1, rows 16 (I & 1) + 0..15
+    // of the slot, lane l row 16 (I & 1) + (l >> 2), chunk l & 3: 1 KB of one
+    // panel in global memory and in LDS (no swizzle: a transposing read of 16
+    // lanes covers 4 consecutive 64-byte rows, 64 distinct banks per 32
+    // lanes). The q offset moves two panels.
     const int row_n = 16 * wave + (lane >> 2), row_t = 2 * wave + (lane >> 5);
-    const int voff_n = row_n * ldb + (((lane & 3) ^ lds_swz(row_n)) << 4);
+    const int ldn = kPQ ? kSlotRowBytes : ldb;
+    const int voff_n = row_n * ldn + (((lane & 3) ^ lds_swz(row_n)) << 4);
     const int voff_t = row_t * ldb + (((lane & 31) ^ tr_swz(row_t)) << 4);
-    const int voff_p = kTP ? voff_t : voff_n;
-    const int voff_q = kTQ ? voff_t : voff_n;
+    const int voff_pt = (wave >> 1) * panb + (16 * (wave & 1) + (lane >> 2)) * kSlotRowBytes + ((lane & 3) << 4);
+    const int voff_p = kPT ? voff_pt : kTP ? voff_t : voff_n;
+    const int voff_q = kPT ? voff_pt : kTQ ? voff_t : voff_n;
 
     // In the bf16 update, slots sb .. sb + 7 are this tile's own 256 rows.
     // Slot positions past the end (s >= ns) are loads that nobody reads but
@@ -1058,10 +1115,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         for (int q = q0; q < q1; ++q) {
             const int soff_t = s >= ns ? soff_end : (s * 32 + 8 * q) * ldb;
             const int soff_n = s >= ns ? soff_end : s * kSlotRowBytes + q * 64 * ldb;
+            const int soff_pt = s >= ns ? soff_end : 2 * q * panb + s * 32 * kSlotRowBytes;
+            const int soff_pq = s >= ns ? soff_end : s * panb + q * 64 * kSlotRowBytes;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, voff_p, kTP ? soff_t : soff_n, 0, 0);
+                rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, voff_p, kPT ? soff_pt : kTP ? soff_t : soff_n,
+                0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rq, (lds_ptr_t)(sp + kSlotOpBytes + (wave + 4 * q) * 1024), 16, voff_q, kTQ ? soff_t : soff_n, 0, 0);
+                rq, (lds_ptr_t)(sp + kSlotOpBytes + (wave + 4 * q) * 1024), 16, voff_q,
+                kPT ? soff_pt : kPQ ? soff_pq : kTQ ? soff_t : soff_n, 0, 0);
         }
     };
 
@@ -1083,10 +1144,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // k-step ks and half e only add whole rows (ks * 8192 + e * 2048 bytes).
     // Both layouts give lane l the k values 16 ks + 8 (l >> 5) + 0..7 of its
     // row or column, so they can be mixed.
+    // Panel k-rows: the same lane -> (row, column) map; column cl sits in
+    // panel cl >> 5, rows of 64 bytes, so k-step ks adds 1 KB and half e 256 B.
     auto off_t = [&](int base) {
         const int g = lane >> 4, x = lane & 15;
         const int kr = 8 * (g >> 1) + (x >> 2);
         const int cl = base + 16 * (g & 1) + 4 * (x & 3);
+        if (kPT)
+            return (cl >> 5) * (32 * kSlotRowBytes) + kr * kSlotRowBytes + (((cl >> 3) & 3) << 4) + (cl & 7) * 2;
         return kr * kTrRowBytes + (((cl >> 3) ^ tr_swz(kr)) << 4) + (cl & 7) * 2;
     };
     int aoff[4], boff[4];
@@ -1095,10 +1160,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         aoff[i] = kTP ? off_t(wr * 128 + i * 32) : lds_off(wr * 128 + i * 32 + fr, fg);
         boff[i] = kSlotOpBytes + (kTQ ? off_t(wc * 128 + i * 32) : lds_off(wc * 128 + i * 32 + fr, fg));
     }
+    constexpr int kTrStep = kPT ? 16 * kSlotRowBytes : 16 * kTrRowBytes;   // 16 k-rows
+    constexpr int kTrHalf = kPT ? 4 * kSlotRowBytes : 4 * kTrRowBytes;     // 4 k-rows
     auto read_frag = [&](const char* sp, int off, int ks, bool tr) __attribute__((always_inline)) {
         if (tr) {
-            const uint2 v0 = ds_read_tr(sp + off + ks * 8192);
-            const uint2 v1 = ds_read_tr(sp + off + ks * 8192 + 2048);
+            const uint2 v0 = ds_read_tr(sp + off + ks * kTrStep);
+            const uint2 v1 = ds_read_tr(sp + off + ks * kTrStep + kTrHalf);
             return make_uint4(v0.x, v0.y, v1.x, v1.y);
         }
         return *reinterpret_cast<const uint4*>(sp + (off ^ (ks << 5)));
