@@ -62,12 +62,33 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
 __device__ __forceinline__ float to_f32(float v) { return v; }
 
+// Global-memory view of a pointer. Caller buffers and the workspace are all
+// device memory, but pointers read from descriptors are generic, and generic
+// accesses compile to flat instructions, which count on both the vector
+// memory and the LDS counters and may complete out of order with other
+// loads: a kernel that waits for its LDS traffic (s_waitcnt lgkmcnt) then
+// also waits for every flat store still in flight, and the compiler's own
+// waits for a flat load become vmcnt(0), i.e. for every LDS DMA issued after
+// it. The GEMM kernels therefore address global memory through this cast.
+#define NS_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ NS_GLOBAL T* gbl(T* p)
+{
+    return (NS_GLOBAL T*)p;
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte global store (p 16-byte aligned)
+__device__ __forceinline__ void st16(void* p, uint4 v)
+{
+    *(NS_GLOBAL u32x4*)gbl(p) = u32x4{v.x, v.y, v.z, v.w};
+}
+
 // Row r of a caller matrix: contiguous rows of `cols` elements from `user`,
 // or the row table's entry when the matrix came as row blocks.
 template <typename T>
 __device__ __forceinline__ T* grow(void* user, void* const* tab, int64_t cols, int64_t r)
 {
-    return tab ? static_cast<T*>(tab[r]) : static_cast<T*>(user) + r * cols;
+    return tab ? static_cast<T*>(gbl(tab)[r]) : static_cast<T*>(user) + r * cols;
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
@@ -75,25 +96,25 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 
 // Four consecutive elements from four fp32 values (8-byte bf16 / 16-byte fp32
-// store; the caller guarantees alignment).
+// store to global memory; the caller guarantees alignment).
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d)
 {
     bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-    *reinterpret_cast<bf16x4*>(p) = v;
+    *(NS_GLOBAL bf16x4*)gbl(p) = v;
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d)
 {
     f32x4 v = {a, b, c, d};
-    *reinterpret_cast<f32x4*>(p) = v;
+    *(NS_GLOBAL f32x4*)gbl(p) = v;
 }
 __device__ __forceinline__ f32x4 load4(const bf16* p)
 {
-    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 v = *(NS_GLOBAL const bf16x4*)gbl(p);
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 __device__ __forceinline__ f32x4 load4(const float* p)
 {
-    return *reinterpret_cast<const f32x4*>(p);
+    return *(NS_GLOBAL const f32x4*)gbl(p);
 }
 
 // Butterfly sum over the 64 lanes of a wavefront (same order on every lane).
@@ -613,7 +634,7 @@ __device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld
     for (int q = 0; q < 32; ++q) {
         const int R = wave * 64 + 2 * q + half;
         const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
-        *reinterpret_cast<uint4*>(dst + R * ld + 8 * (p ^ (R & 31))) = v;
+        st16(dst + R * ld + 8 * (p ^ (R & 31)), v);
     }
 }
 
@@ -633,7 +654,7 @@ __device__ __forceinline__ void tile_store_pan(const char* ws, bf16* xt, int64_t
         const int rb = q >> 3, pp = q & 7;
         const int R = wave * 64 + 16 * rb + g + 4 * a;
         const uint4 v = *reinterpret_cast<const uint4*>(ws + (R & 63) * 512 + (((4 * pp + b) ^ (R & 31)) << 4));
-        *reinterpret_cast<uint4*>(xt + ((pc0 + pp) * np + r0 + R) * kPanelCols + 8 * b) = v;
+        st16(xt + ((pc0 + pp) * np + r0 + R) * kPanelCols + 8 * b, v);
     }
 }
 
@@ -654,13 +675,13 @@ __device__ __forceinline__ void tile_store_user(const char* ws, bf16* user, void
         if (row < nrows) {
             bf16* dst = grow<bf16>(user, rows_tab, cols, row) + c0;
             if (c0 + 8 <= ncols && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                *reinterpret_cast<uint4*>(dst) = v;
+                st16(dst, v);
             } else {
                 const bf16x8 h = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     if (c0 + e < ncols)
-                        dst[e] = h[e];
+                        gbl(dst)[e] = h[e];
             }
         }
     }
@@ -832,7 +853,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
                     const auto sy = __builtin_amdgcn_permlane32_swap(l2[2 * h].y, l2[2 * h + 1].y, false, false);
                     const uint4 v = make_uint4(sx[0], sy[0], sx[1], sy[1]);
                     const int r = wr * 128 + i * 32 + 16 * h + 8 * fg;
-                    *reinterpret_cast<uint4*>(lo_g + (int64_t)c * ldt + r) = v;
+                    st16(lo_g + (int64_t)c * ldt + r, v);
                 }
             }
         }
@@ -892,13 +913,13 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
     if constexpr (STAGE == 1) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            dcol[j] = M.adiag[gbj + wc * 128 + j * 32 + fr];
+            dcol[j] = gbl(M.adiag)[gbj + wc * 128 + j * 32 + fr];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg)
                 drows[i][rg] =
-                    *reinterpret_cast<const f32x4*>(M.adiag + gbi + wr * 128 + i * 32 + rg * 8 + fg * 4);
+                    *(NS_GLOBAL const f32x4*)gbl(M.adiag + gbi + wr * 128 + i * 32 + rg * 8 + fg * 4);
     }
     // Every wavefront is done with the ring; each has waited for its own
     // block loads (STAGE 1) at the end of the K loop.
@@ -954,7 +975,7 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
                             if (r == c) {
                                 if constexpr (STAGE == 1)
                                     x = fmaf(cb, drow[rg][e], x);
-                                dout[gbi + c] = x - (float)(bf16)x;
+                                gbl(dout)[gbi + c] = x - (float)(bf16)x;
                             }
                             const bf16 h = (bf16)x;
                             *reinterpret_cast<bf16*>(tile_at(cslot, c, r)) = h;
@@ -1226,7 +1247,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     if constexpr (kIdent) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            rowscale[ii] = ca + M.bdiag[gbi + wr * 128 + ii * 32 + fr];
+            rowscale[ii] = ca + gbl(M.bdiag)[gbi + wr * 128 + ii * 32 + fr];
     }
     // peel slot P, k-step ks of the slot
     auto ident = [&](int P, int ks, const uint4 (&bfr)[4]) {
@@ -1315,14 +1336,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         }
     };
 
-    // (the epilogue block's quarter 3 first: the oldest loads, so the wait
-    // counts below, which only bound the number of younger loads, still hold)
+    // The epilogue block's quarter 3 goes out right after slot 0: the first
+    // wait is for slot 0 alone (16 younger loads without it, 24 with it), and
+    // from step 0 on it is older than every slot waited for, so the wait
+    // counts in the loop, which bound the number of younger loads, still hold.
+    issue(sl0, 0);
     if constexpr (kPre)
         issue_blk_quarter(pre_blk, M.ldt, lo3, 3, wave, lane);
-    issue(sl0, 0);
     issue(sl1, 1);
     issue(sl2, 2);
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    if constexpr (kPre)
+        asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
     read_frags(sl0, 0, fa, fb);
     // Every tile visits the slots in the same order, so tiles that share an
     // operand block read the same k-slice at about the same time (L2 reuse);
@@ -1353,7 +1379,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         for (; s < ns; s += 4)
             ring(s, Peel<-1>{}, Peel<-1>{}, Peel<-1>{}, Peel<-1>{});
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // (the builtin, not inline asm: the compiler's own wait insertion then
+    // knows that no LDS DMA is in flight and adds no waits before the
+    // epilogues' LDS writes; 0x0F70 = vmcnt(0), other counters untouched)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
 
     // Epilogues. Lane l, block (i, j), register group rg holds rows
     // lr0..lr0+3 of column lc (tile-local).
@@ -1406,7 +1437,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                     if (!diag) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            out[(r0 + e) * ld + c] = from_f32<OpT>(v[e]);
+                            gbl(out)[(r0 + e) * ld + c] = from_f32<OpT>(v[e]);
                         store4(out + c * ld + r0, v[0], v[1], v[2], v[3]);
                     } else {
                         // Diagonal tile: take the upper triangle and mirror it,
@@ -1414,8 +1445,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             if (lr0 + e < lc) {
-                                out[(r0 + e) * ld + c] = from_f32<OpT>(v[e]);
-                                out[c * ld + r0 + e] = from_f32<OpT>(v[e]);
+                                gbl(out)[(r0 + e) * ld + c] = from_f32<OpT>(v[e]);
+                                gbl(out)[c * ld + r0 + e] = from_f32<OpT>(v[e]);
                             }
                         }
                     }
@@ -1435,8 +1466,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                 const int64_t rc = gbi + wr * 128 + i * 32 + fr;
                 if (has) {
                     if (STAGE == 1)
-                        v = cb * to_f32(ain[rc * ld + rc]) + cc * v;
-                    out[rc * ld + rc] = from_f32<OpT>(v);
+                        v = cb * to_f32(gbl(ain)[rc * ld + rc]) + cc * v;
+                    gbl(out)[rc * ld + rc] = from_f32<OpT>(v);
                 }
             }
         }
@@ -1473,13 +1504,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
                     store4(xt + c * ldt + r0, y[0], y[1], y[2], y[3]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        xb[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
+                        gbl(xb)[(r0 + e) * ldx + c] = from_f32<OpT>(y[e]);
                 } else if (c < M.n) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         if (r0 + e < M.m) {
                             OpT* row = grow<OpT>(user, M.rows_tab, M.cols, M.trans ? c : r0 + e);
-                            row[M.trans ? r0 + e : c] = from_f32<OpT>(y[e]);
+                            gbl(row)[M.trans ? r0 + e : c] = from_f32<OpT>(y[e]);
                         }
                     }
                 }
