@@ -123,8 +123,20 @@ def test_moe_mixed_batch():
         else:
             dev.append(torch.randn(s, generator=gen, device="cuda").to(torch.bfloat16))
     inputs = {i: dev[i].cpu() for i in idx}
+    orig = [d.clone() for d in dev]
     ns.orthogonalize(dev)
     torch.cuda.synchronize()
+    # A seeded permutation of the same batch: every matrix gives the same
+    # bits wherever it sits (the cost order's ties, the tile lists and the
+    # workspace placement all change).
+    perm = np.random.default_rng(1004).permutation(len(shapes))
+    permuted = [orig[j] for j in perm]
+    del orig
+    ns.orthogonalize(permuted)
+    torch.cuda.synchronize()
+    for k, j in enumerate(perm):
+        assert torch.equal(permuted[k].view(torch.int16), dev[j].view(torch.int16)), (k, int(j))
+    del permuted
     for y in dev[::7]:
         assert bool(torch.isfinite(y).all())
     for i in idx:
