@@ -7,6 +7,13 @@ normalize/transpose, 5 x (X X^T, bA + cA^2, aX + BX), write-back.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+Workloads: dense_lowrank (default), ragged_remainder_R (R of the remainder
+pool's 8192x6144 matrices, the last one passed through 64 row shards),
+moe_mixed (130 matrices of four shapes), attn_gate (32 x 18x2304 passed as 8
+padded row shards each) and tiny_fp32 (4 x 64x32 fp32). The last two run in
+the fused small-matrix kernel: fp32 arithmetic on the vector ALUs, reported
+against the fp32 vector peak.
+
 Prints one JSON line. `value` is matrices per second with the inputs already
 resident in HBM; FLOPs per matrix follow 5 * (4 m^2 n + 2 m^3), m = min dim.
 Every timed step works on its own resident copy of the batch (restored from a
@@ -23,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NS-orthogonalized matrices/s + TFLOP/s (% bf16 MFMA peak), 8192x6144 bf16"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector (the fused small-matrix kernel)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -42,6 +50,18 @@ def make_workload(name):
         mats = [c.mat for c in wl.ragged_remainder(r, world=64, padded=True)]
         desc = {"workload": name, "matrices": r, "shape": [8192, 6144], "dtype": "bf16",
                 "input": "N(0,1), seed 3", "ns_steps": 5}
+    elif name == "attn_gate":
+        # the 32 attention-gate matrices of 18 x 2304, each passed as its 8
+        # row shards padded to 3 rows (24 x 2304, rows 18..23 zero)
+        cases = wl.attn_gate()
+        mats = [c.mat for c in cases]
+        desc = {"workload": "attn_gate", "matrices": len(mats), "shape": [24, 2304], "real_shape": [18, 2304],
+                "dtype": "bf16", "input": "0.02*N(0,1), seed 1, 8 row shards (3,3,3,3,3,3,0,0) padded to 3 rows",
+                "ns_steps": 5}
+    elif name == "tiny_fp32":
+        mats = [c.mat for c in wl.tiny_fp32()]
+        desc = {"workload": "tiny_fp32", "matrices": len(mats), "shape": [64, 32], "dtype": "fp32",
+                "input": "N(0,1), seed 0, matrix 3 rows 56..63 zero", "ns_steps": 5}
     elif name == "moe_mixed":
         g = torch.Generator(device="cuda").manual_seed(4)
         mats = [torch.randn(s, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
@@ -73,6 +93,22 @@ def cpu_baseline(sample_rows=6144, sample_cols=4608):
             "kind": "oracle", "gflops_fp64": round(flops / dt / 1e9, 3), "seconds": round(dt, 2),
             "sample": f"1 NS step of the top-left {sample_rows}x{sample_cols} block of matrix 0 "
                       f"(fp64, plain loops + OpenMP), scaled by metric FLOPs to 8192x6144 x 5 steps"}
+
+
+def cpu_baseline_small(mats, real_shape=None):
+    """The fp64 oracle, as it stands, on the whole batch of a small-matrix
+    workload (milliseconds of CPU work per matrix)."""
+    from newton_schulz_04_amd import workloads as wl
+    from oracle import oracle
+    t0 = time.time()
+    for g in mats:
+        oracle.newton_schulz(g.float().numpy(), steps=5, coeffs=oracle.QUINTIC)
+    dt = time.time() - t0
+    flops = sum(wl.flops_per_matrix(*(real_shape or tuple(g.shape))) for g in mats)
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": round(len(mats) / dt, 3), "unit": "matrices/s", "cores": cores, "kind": "oracle",
+            "gflops_fp64": round(flops / dt / 1e9, 3), "seconds": round(dt, 3),
+            "sample": f"the whole batch ({len(mats)} matrices, 5 steps each)"}
 
 
 def metric_flops_per_kind(shapes):
@@ -137,7 +173,12 @@ def main():
     log(f"library {ns.version()}; generating workload {args.workload}")
     mats, desc = make_workload(args.workload)
     shapes = [tuple(m.shape) for m in mats]
-    flops_batch = sum(wl.flops_per_matrix(r, c) for r, c in shapes)
+    # metric FLOPs on the real shape (the attention gate's 18 x 2304, not
+    # its padded 24 x 2304)
+    real = tuple(desc.get("real_shape", ())) or None
+    flops_batch = sum(wl.flops_per_matrix(*(real or (r, c))) for r, c in shapes)
+    small_batch = all(min(r, c) <= 32 for r, c in shapes)
+    cpu_mats = [m.clone() for m in mats] if small_batch else None
     pristine = [m.cuda() for m in mats]
     del mats
     nbatch = max(1, min(args.steps, 16))
@@ -176,8 +217,22 @@ def main():
         if kind in per_kind and per_kind[kind]:
             entry["tflops"] = round(per_kind[kind] / (avg * 1e-3) / 1e12, 1)
         kernels[kind] = entry
-    dom = max((k for k in kernels if k in per_kind), key=lambda k: kernels[k]["ms_total"])
-    achieved = per_kind[dom] / (kernels[dom]["ms_avg"] * 1e-3) / 1e12
+    if small_batch:
+        # one fused kernel does the whole iteration in fp32 on the vector
+        # ALUs: metric FLOPs of the padded batch per launch against the fp32
+        # vector peak
+        dom = "small"
+        achieved = sum(wl.flops_per_matrix(r, c) for r, c in shapes) / (kernels[dom]["ms_avg"] * 1e-3) / 1e12
+        roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
+                    "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_FP32_VALU_TFLOPS, 5), "traffic": None}
+    else:
+        dom = max((k for k in kernels if k in per_kind), key=lambda k: kernels[k]["ms_total"])
+        achieved = per_kind[dom] / (kernels[dom]["ms_avg"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(args.workload, dom)}
     ms_per_step = elapsed / args.steps * 1e3
     tflops = flops_batch / (elapsed / args.steps) / 1e12
     value = len(shapes) * args.steps / elapsed
@@ -192,21 +247,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if small_batch else "bf16",
         "data": "synthetic",
         "config": desc,
         "tflops": round(tflops, 1),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload, dom)},
+        "roofline": roofline,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         try:
             log("timing the CPU oracle on a bounded sample")
-            out["cpu_baseline"] = cpu_baseline()
+            out["cpu_baseline"] = cpu_baseline_small(cpu_mats, real) if small_batch else cpu_baseline()
         except Exception as e:  # the oracle is optional for the GPU figure
             out["cpu_baseline"] = {"error": str(e)}
     print(json.dumps(out), flush=True)

@@ -16,6 +16,7 @@
 // hipEventQuery, never waited on).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <limits>
@@ -446,8 +447,13 @@ ns_status run(Context* c, const int64_t* shapes, const Layout& L, int32_t count,
         for (int s = 0; s < (per_step ? steps : (steps > 0 ? 1 : 0)); ++s)
             for (int k = 0; k < 3; ++k)
                 table.v[s][k] = coef(s, k);
+        int xl = 0;
+        for (int32_t idx : p.small) {
+            const ns::PlanMat& pm = p.mats[idx];
+            xl = std::max(xl, ns::small_xl_floats(pm.m, pm.n));
+        }
         e = timed(ns::kKindSmall, stream, [&] {
-            return ns::launch_small(dtype, small, (int)p.small.size(), steps, table, stream);
+            return ns::launch_small(dtype, small, (int)p.small.size(), steps, table, xl, stream);
         });
         if (e != hipSuccess)
             return hip_fail(e, "small-matrix kernel launch");

@@ -9,9 +9,12 @@
 namespace ns {
 
 // Fused whole-iteration kernel for matrices with min dim <= kSmallMax, one
-// workgroup per matrix, fp32 arithmetic.
+// workgroup per matrix, fp32 arithmetic. X stays in LDS for matrices whose
+// small_xl_floats(m, n) is nonzero and at most `xl_floats` (the launch's LDS
+// share for it: the largest such value in the batch, or 0).
+int small_xl_floats(int m, int n);
 hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
-                        const CoeffTable& coeffs, hipStream_t stream);
+                        const CoeffTable& coeffs, int xl_floats, hipStream_t stream);
 
 // Sum of squares of each large matrix in kNormChunk pieces (one workgroup per
 // piece) ...

@@ -157,42 +157,75 @@ __device__ __forceinline__ int find_mat(const int32_t* prefix, int nmats, int b)
 //               partial A's are added in wavefront order.
 //   B = bA + cA^2 in LDS.
 //   X <- aX + BX column by column; thread t owns columns t, t+256, ...
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__ mats,
-                                                    int steps, const CoeffTable coeffs)
+// The fused small-matrix path (m <= 32). One workgroup per matrix runs the
+// whole iteration in fp32; X stays resident in LDS when it fits (column-major,
+// MR + 1 floats per column), else in an L2-resident workspace buffer that the
+// Gram pass streams through LDS in chunks of kSmallChunk columns, the next
+// chunk's loads in flight while the current one is multiplied. MR is m
+// rounded up to a multiple of 8: rows m .. MR - 1 are zero throughout, so
+// every product below is the exact m x m / m x n one plus zeros. Every sum
+// runs in a fixed order that depends only on (m, n).
+constexpr int kSmallThreads = 512;                // 8 wavefronts, 2 per SIMD
+constexpr int kSmallChunk = 128;
+constexpr int kSmallPartFloats = 8192;            // G x MR x MR Gram partials
+constexpr int kSmallSqFloats = 2 * 32 * 33;       // A and B, MR x (MR + 1)
+constexpr int kSmallXlMaxFloats = 28672;          // X resident in LDS up to 112 KB (156 KB in all)
+static_assert(4 * (kSmallPartFloats + kSmallSqFloats + 8 + kSmallXlMaxFloats) <= 160 * 1024,
+              "small-matrix kernel LDS exceeds the 160 KB of a compute unit");
+
+template <int DT, int MR, bool XL>
+__device__ __forceinline__ void small_body(const SmallMat& S, int steps, const CoeffTable& coeffs, float* lds)
 {
     using T = typename Elt<DT>::type;
-    __shared__ float red[4];
-    __shared__ float xs[64][33];
-    __shared__ float part[4][32][33];
-    __shared__ float as[32][33];
-    __shared__ float bs[32][33];
+    constexpr int LD = MR + 1;                    // column pitch of X in LDS
+    constexpr int NB = MR / 4;                    // 4 x 4 Gram blocks per edge
+    constexpr int NBLK = NB * NB;
+    constexpr int G = kSmallThreads / NBLK;       // column groups of the Gram pass
+    constexpr int QL = MR * kSmallChunk / kSmallThreads;   // chunk loads per thread
+    float* part = lds;                            // [G][MR][MR]
+    float* as = lds + kSmallPartFloats;           // [MR][LD]
+    float* bs = as + MR * LD;                     // [MR][LD]
+    float* red = lds + kSmallPartFloats + kSmallSqFloats;
+    float* xs = red + 8;                          // X (XL) or one chunk, [cols][LD]
 
-    const SmallMat S = mats[blockIdx.x];
     const int tid = threadIdx.x;
     const int m = S.m, n = S.n;
     const int64_t cols = S.cols;
     T* g = static_cast<T*>(S.user);
-    float* xw = S.xw;
+    NS_GLOBAL float* xw = gbl(S.xw);
+    auto gat = [&](int64_t r) { return gbl(grow<T>(g, S.rows_tab, cols, r)); };
 
-    // ||G||_F over G's own row-major order: thread t takes elements t, t+256, ...
+    // ||G||_F over G's own row-major order: thread t takes elements t, t+512, ...
     const int64_t numel = S.rows * S.cols;
     float s = 0.f;
-    for (int64_t e = tid; e < numel; e += kThreads) {
-        const float v = to_f32(S.rows_tab ? grow<T>(g, S.rows_tab, cols, e / cols)[e % cols] : g[e]);
+    for (int64_t e = tid; e < numel; e += kSmallThreads) {
+        const float v = to_f32(gat(e / cols)[e % cols]);
         s = fmaf(v, v, s);
     }
-    const float inv = 1.f / (sqrtf(block_sum(s, red)) + kEps);
-
-    for (int e = tid; e < m * n; e += kThreads) {
+    s = wave_sum(s);
+    if ((tid & 63) == 0)
+        red[tid >> 6] = s;
+    __syncthreads();
+    s = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+    const float inv = 1.f / (sqrtf(s) + kEps);
+    // X = G inv, oriented m x n (rows MR - m .. stay zero)
+    for (int e = tid; e < MR * n; e += kSmallThreads) {
         const int i = e / n, j = e - (e / n) * n;
-        const float v = to_f32(S.trans ? grow<T>(g, S.rows_tab, cols, j)[i] : grow<T>(g, S.rows_tab, cols, i)[j]);
-        xw[e] = v * inv;
+        float v = 0.f;
+        if (i < m)
+            v = to_f32(S.trans ? gat(j)[i] : gat(i)[j]) * inv;
+        if (XL)
+            xs[j * LD + i] = v;
+        else if (i < m)
+            xw[e] = v;
     }
     __syncthreads();
 
-    const int tt = tid & 63, kg = tid >> 6;
-    const int ti = tt >> 3, tj = tt & 7;
+    const int blk = tid % NBLK, kg = tid / NBLK;
+    const int ti = blk / NB, tj = blk % NB;
+    const bool gram = kg < G;
+    // X <- aX + BX: RG threads share a column, each taking MR / RG rows
+    const int RG = XL ? (n <= 128 ? 4 : (n <= 256 ? 2 : 1)) : 1;
     for (int step = 0; step < steps; ++step) {
         const bool last = step == steps - 1;
         const float* co = coeffs.v[coeffs.per_step ? step : 0];
@@ -203,87 +236,154 @@ __global__ __launch_bounds__(kThreads) void k_small(const SmallMat* __restrict__
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 acc[p][q] = 0.f;
-        for (int j0 = 0; j0 < n; j0 += 64) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int idx = tid + kThreads * q;
-                const int r = idx >> 6, jj = idx & 63;
-                xs[jj][r] = (r < m && j0 + jj < n) ? xw[r * n + j0 + jj] : 0.f;
-            }
-            __syncthreads();
-            for (int jj = kg; jj < 64; jj += 4) {
-                float xr[4], xc[4];
+        auto gram_cols = [&](const float* xc, int ncols) __attribute__((always_inline)) {
+            if (!gram)
+                return;
+            for (int jj = kg; jj < ncols; jj += G) {
+                float xr[4], xq[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    xr[p] = xs[jj][4 * ti + p];
-                    xc[p] = xs[jj][4 * tj + p];
+                    xr[p] = xc[jj * LD + 4 * ti + p];
+                    xq[p] = xc[jj * LD + 4 * tj + p];
                 }
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        acc[p][q] = fmaf(xr[p], xc[q], acc[p][q]);
+                        acc[p][q] = fmaf(xr[p], xq[q], acc[p][q]);
             }
-            __syncthreads();
+        };
+        if (XL) {
+            gram_cols(xs, n);
+        } else {
+            // chunk c of X: element e = tid + 256 q is row e / CH, column e % CH
+            float pf[QL];
+            auto fetch = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+                for (int q = 0; q < QL; ++q) {
+                    const int e = tid + kSmallThreads * q, r = e / kSmallChunk, jj = e % kSmallChunk;
+                    pf[q] = (r < m && j0 + jj < n) ? xw[(int64_t)r * n + j0 + jj] : 0.f;
+                }
+            };
+            fetch(0);
+            for (int j0 = 0; j0 < n; j0 += kSmallChunk) {
+#pragma unroll
+                for (int q = 0; q < QL; ++q) {
+                    const int e = tid + kSmallThreads * q;
+                    xs[(e % kSmallChunk) * LD + e / kSmallChunk] = pf[q];
+                }
+                __syncthreads();
+                if (j0 + kSmallChunk < n)
+                    fetch(j0 + kSmallChunk);
+                gram_cols(xs, kSmallChunk);
+                __syncthreads();
+            }
         }
+        if (gram) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+            for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                part[kg][4 * ti + p][4 * tj + q] = acc[p][q];
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + kThreads * q, r = e >> 5, c = e & 31;
-            as[r][c] = ((part[0][r][c] + part[1][r][c]) + part[2][r][c]) + part[3][r][c];
+                for (int q = 0; q < 4; ++q)
+                    part[(kg * MR + 4 * ti + p) * MR + 4 * tj + q] = acc[p][q];
         }
         __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + kThreads * q, r = e >> 5, c = e & 31;
+        for (int e = tid; e < MR * MR; e += kSmallThreads) {
+            float v = part[e];
+            for (int k = 1; k < G; ++k)
+                v += part[k * MR * MR + e];
+            as[(e / MR) * LD + e % MR] = v;
+        }
+        __syncthreads();
+        for (int e = tid; e < MR * MR; e += kSmallThreads) {
+            const int r = e / MR, c = e % MR;
             float aa = 0.f;
 #pragma unroll
-            for (int t = 0; t < 32; ++t)
-                aa = fmaf(as[r][t], as[t][c], aa);
-            bs[r][c] = cb * as[r][c] + cc * aa;
+            for (int t = 0; t < MR; ++t)
+                aa = fmaf(as[r * LD + t], as[t * LD + c], aa);
+            bs[r * LD + c] = cb * as[r * LD + c] + cc * aa;
         }
         __syncthreads();
-        for (int j = tid; j < n; j += kThreads) {
-            float x[32];
+        // X <- aX + BX, column by column (the next column's loads in flight)
+        const int rg = tid % RG;
+        constexpr int MAXR = MR;
+        const int r0 = rg * (MR / RG), r1 = r0 + MR / RG;
+        const int jstep = kSmallThreads / RG;
+        float xn[MR];
+        auto load_col = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
-            for (int r = 0; r < 32; ++r)
-                x[r] = r < m ? xw[r * n + j] : 0.f;
+            for (int r = 0; r < MR; ++r)
+                xn[r] = j < n ? (XL ? xs[j * LD + r] : (r < m ? xw[(int64_t)r * n + j] : 0.f)) : 0.f;
+        };
+        int j = tid / RG;
+        load_col(j);
+        for (; j < n; j += jstep) {
+            float x[MAXR];
 #pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                if (r < m) {
+            for (int r = 0; r < MR; ++r)
+                x[r] = xn[r];
+            // (a column is read and rewritten only by its RG lanes, one
+            // wavefront, loads before stores; the next column is this
+            // thread's own)
+            load_col(j + jstep);
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                if (r >= r0 && r < r1 && r < m) {
                     float y = ca * x[r];
 #pragma unroll
-                    for (int t = 0; t < 32; ++t)
-                        y = fmaf(bs[r][t], x[t], y);
-                    if (!last)
-                        xw[r * n + j] = y;
-                    else if (S.trans)
-                        grow<T>(g, S.rows_tab, cols, j)[r] = from_f32<T>(y);
-                    else
-                        grow<T>(g, S.rows_tab, cols, r)[j] = from_f32<T>(y);
+                    for (int t = 0; t < MR; ++t)
+                        y = fmaf(bs[r * LD + t], x[t], y);
+                    if (!last) {
+                        if (XL)
+                            xs[j * LD + r] = y;
+                        else
+                            xw[(int64_t)r * n + j] = y;
+                    } else if (S.trans) {
+                        gat(j)[r] = from_f32<T>(y);
+                    } else {
+                        gat(r)[j] = from_f32<T>(y);
+                    }
                 }
             }
         }
         __syncthreads();
     }
     if (steps == 0) {
-        for (int e = tid; e < m * n; e += kThreads) {
-            const int i = e / n, j = e - (e / n) * n;
-            T* row = S.trans ? grow<T>(g, S.rows_tab, cols, j) : grow<T>(g, S.rows_tab, cols, i);
-            row[S.trans ? i : j] = from_f32<T>(xw[e]);
+        for (int e = tid; e < m * n; e += kSmallThreads) {
+            const int i = e / n, jj = e - (e / n) * n;
+            const float v = XL ? xs[jj * LD + i] : xw[e];
+            if (S.trans)
+                gat(jj)[i] = from_f32<T>(v);
+            else
+                gat(i)[jj] = from_f32<T>(v);
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// Norm, pass 1: one workgroup per kNormChunk elements of G (row-major). Thread
-// t accumulates elements (t + 256 q) * V + e, q outer, e inner, V = 16 bytes
-// of elements; lanes fold by butterfly, wavefronts in order.
+template <int DT>
+__global__ __launch_bounds__(kSmallThreads) void k_small(const SmallMat* __restrict__ mats, int steps,
+                                                    const CoeffTable coeffs, int xl_floats)
+{
+    extern __shared__ float lds[];
+    const SmallMat S = mats[blockIdx.x];
+    const int mr = (S.m + 7) & ~7;
+    // X resident in LDS when its n x (MR + 1) floats fit the launch's share
+    const bool xl = (int64_t)S.n * (mr + 1) <= xl_floats;
+    switch (mr) {
+    case 8:
+        xl ? small_body<DT, 8, true>(S, steps, coeffs, lds) : small_body<DT, 8, false>(S, steps, coeffs, lds);
+        break;
+    case 16:
+        xl ? small_body<DT, 16, true>(S, steps, coeffs, lds) : small_body<DT, 16, false>(S, steps, coeffs, lds);
+        break;
+    case 24:
+        xl ? small_body<DT, 24, true>(S, steps, coeffs, lds) : small_body<DT, 24, false>(S, steps, coeffs, lds);
+        break;
+    default:
+        xl ? small_body<DT, 32, true>(S, steps, coeffs, lds) : small_body<DT, 32, false>(S, steps, coeffs, lds);
+        break;
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_norm_partial(const LargeMat* __restrict__ mats,
                                                            int nmats,
@@ -1550,13 +1650,36 @@ hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, in
 
 }  // namespace
 
-hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
-                        const CoeffTable& coeffs, hipStream_t stream)
+int small_lds_floats(int max_xl_floats)
 {
+    const int x_area = max_xl_floats > kSmallChunk * 33 ? max_xl_floats : kSmallChunk * 33;
+    return kSmallPartFloats + kSmallSqFloats + 8 + x_area;
+}
+
+int small_xl_floats(int m, int n)
+{
+    const int64_t need = (int64_t)n * (((m + 7) & ~7) + 1);
+    return need <= kSmallXlMaxFloats ? (int)need : 0;
+}
+
+hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
+                        const CoeffTable& coeffs, int xl_floats, hipStream_t stream)
+{
+    const size_t lds = sizeof(float) * (size_t)small_lds_floats(xl_floats);
+    static bool attr[2] = {false, false};
+    if (!attr[dtype]) {
+        const size_t max_lds = sizeof(float) * (size_t)small_lds_floats(kSmallXlMaxFloats);
+        const hipError_t e = dtype == 0
+            ? hipFuncSetAttribute((const void*)k_small<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds)
+            : hipFuncSetAttribute((const void*)k_small<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
+        if (e != hipSuccess)
+            return e;
+        attr[dtype] = true;
+    }
     if (dtype == 0)
-        hipLaunchKernelGGL(k_small<0>, dim3(count), dim3(kThreads), 0, stream, mats, steps, coeffs);
+        hipLaunchKernelGGL(k_small<0>, dim3(count), dim3(kSmallThreads), lds, stream, mats, steps, coeffs, xl_floats);
     else
-        hipLaunchKernelGGL(k_small<1>, dim3(count), dim3(kThreads), 0, stream, mats, steps, coeffs);
+        hipLaunchKernelGGL(k_small<1>, dim3(count), dim3(kSmallThreads), lds, stream, mats, steps, coeffs, xl_floats);
     return hipGetLastError();
 }
 
