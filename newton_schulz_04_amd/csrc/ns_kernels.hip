@@ -184,7 +184,9 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
     constexpr int QL = MR * kSmallChunk / kSmallThreads;   // chunk loads per thread
     float* part = lds;                            // [G][MR][MR]
     float* as = lds + kSmallPartFloats;           // [MR][LD]
-    float* bs = as + MR * LD;                     // [MR][LD]
+    // B at pitch MR: its reads in X <- aX + BX are the same for every lane,
+    // so 16-byte aligned rows let four of them go as one LDS read
+    float* bs = as + MR * LD;                     // [MR][MR]
     float* red = lds + kSmallPartFloats + kSmallSqFloats;
     float* xs = red + 8;                          // X (XL) or one chunk, [cols][LD]
 
@@ -300,7 +302,7 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
 #pragma unroll
             for (int t = 0; t < MR; ++t)
                 aa = fmaf(as[r * LD + t], as[t * LD + c], aa);
-            bs[r * LD + c] = cb * as[r * LD + c] + cc * aa;
+            bs[r * MR + c] = cb * as[r * LD + c] + cc * aa;
         }
         __syncthreads();
         // X <- aX + BX, column by column (the next column's loads in flight)
@@ -330,8 +332,12 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
                 if (r >= r0 && r < r1 && r < m) {
                     float y = ca * x[r];
 #pragma unroll
-                    for (int t = 0; t < MR; ++t)
-                        y = fmaf(bs[r * LD + t], x[t], y);
+                    for (int t = 0; t < MR; t += 4) {
+                        const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + r * MR + t);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            y = fmaf(b4[u], x[t + u], y);
+                    }
                     if (!last) {
                         if (XL)
                             xs[j * LD + r] = y;
