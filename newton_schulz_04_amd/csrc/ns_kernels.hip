@@ -159,7 +159,7 @@ __device__ __forceinline__ int find_mat(const int32_t* prefix, int nmats, int b)
 //   X <- aX + BX column by column; thread t owns columns t, t+256, ...
 // The fused small-matrix path (m <= 32). One workgroup per matrix runs the
 // whole iteration in fp32; X stays resident in LDS when it fits (column-major,
-// MR + 1 floats per column), else in an L2-resident workspace buffer that the
+// MR + 4 floats per column), else in an L2-resident workspace buffer that the
 // Gram pass streams through LDS in chunks of kSmallChunk columns, the next
 // chunk's loads in flight while the current one is multiplied. MR is m
 // rounded up to a multiple of 8: rows m .. MR - 1 are zero throughout, so
@@ -177,7 +177,8 @@ template <int DT, int MR, bool XL>
 __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const CoeffTable& coeffs, float* lds)
 {
     using T = typename Elt<DT>::type;
-    constexpr int LD = MR + 1;                    // column pitch of X in LDS
+    constexpr int LD = MR + 1;                    // row pitch of A in LDS
+    constexpr int LX = MR + 4;                    // column pitch of X in LDS (16-byte aligned)
     constexpr int NB = MR / 4;                    // 4 x 4 Gram blocks per edge
     constexpr int NBLK = NB * NB;
     constexpr int G = kSmallThreads / NBLK;       // column groups of the Gram pass
@@ -188,7 +189,7 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
     // so 16-byte aligned rows let four of them go as one LDS read
     float* bs = as + MR * LD;                     // [MR][MR]
     float* red = lds + kSmallPartFloats + kSmallSqFloats;
-    float* xs = red + 8;                          // X (XL) or one chunk, [cols][LD]
+    float* xs = red + 8;                          // X (XL) or one chunk, [cols][LX]
 
     const int tid = threadIdx.x;
     const int m = S.m, n = S.n;
@@ -217,7 +218,7 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
         if (i < m)
             v = to_f32(S.trans ? gat(j)[i] : gat(i)[j]) * inv;
         if (XL)
-            xs[j * LD + i] = v;
+            xs[j * LX + i] = v;
         else if (i < m)
             xw[e] = v;
     }
@@ -242,12 +243,8 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
             if (!gram)
                 return;
             for (int jj = kg; jj < ncols; jj += G) {
-                float xr[4], xq[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    xr[p] = xc[jj * LD + 4 * ti + p];
-                    xq[p] = xc[jj * LD + 4 * tj + p];
-                }
+                const f32x4 xr = *reinterpret_cast<const f32x4*>(xc + jj * LX + 4 * ti);
+                const f32x4 xq = *reinterpret_cast<const f32x4*>(xc + jj * LX + 4 * tj);
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
 #pragma unroll
@@ -272,7 +269,7 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
 #pragma unroll
                 for (int q = 0; q < QL; ++q) {
                     const int e = tid + kSmallThreads * q;
-                    xs[(e % kSmallChunk) * LD + e / kSmallChunk] = pf[q];
+                    xs[(e % kSmallChunk) * LX + e / kSmallChunk] = pf[q];
                 }
                 __syncthreads();
                 if (j0 + kSmallChunk < n)
@@ -314,7 +311,7 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
         auto load_col = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
             for (int r = 0; r < MR; ++r)
-                xn[r] = j < n ? (XL ? xs[j * LD + r] : (r < m ? xw[(int64_t)r * n + j] : 0.f)) : 0.f;
+                xn[r] = j < n ? (XL ? xs[j * LX + r] : (r < m ? xw[(int64_t)r * n + j] : 0.f)) : 0.f;
         };
         int j = tid / RG;
         load_col(j);
@@ -340,7 +337,7 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
                     }
                     if (!last) {
                         if (XL)
-                            xs[j * LD + r] = y;
+                            xs[j * LX + r] = y;
                         else
                             xw[(int64_t)r * n + j] = y;
                     } else if (S.trans) {
@@ -356,7 +353,7 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
     if (steps == 0) {
         for (int e = tid; e < m * n; e += kSmallThreads) {
             const int i = e / n, jj = e - (e / n) * n;
-            const float v = XL ? xs[jj * LD + i] : xw[e];
+            const float v = XL ? xs[jj * LX + i] : xw[e];
             if (S.trans)
                 gat(jj)[i] = from_f32<T>(v);
             else
@@ -372,8 +369,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_small(const SmallMat* __restr
     extern __shared__ float lds[];
     const SmallMat S = mats[blockIdx.x];
     const int mr = (S.m + 7) & ~7;
-    // X resident in LDS when its n x (MR + 1) floats fit the launch's share
-    const bool xl = (int64_t)S.n * (mr + 1) <= xl_floats;
+    // X resident in LDS when its n x (MR + 4) floats fit the launch's share
+    const bool xl = (int64_t)S.n * (mr + 4) <= xl_floats;
     switch (mr) {
     case 8:
         xl ? small_body<DT, 8, true>(S, steps, coeffs, lds) : small_body<DT, 8, false>(S, steps, coeffs, lds);
@@ -1658,13 +1655,13 @@ hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, in
 
 int small_lds_floats(int max_xl_floats)
 {
-    const int x_area = max_xl_floats > kSmallChunk * 33 ? max_xl_floats : kSmallChunk * 33;
+    const int x_area = max_xl_floats > kSmallChunk * 36 ? max_xl_floats : kSmallChunk * 36;
     return kSmallPartFloats + kSmallSqFloats + 8 + x_area;
 }
 
 int small_xl_floats(int m, int n)
 {
-    const int64_t need = (int64_t)n * (((m + 7) & ~7) + 1);
+    const int64_t need = (int64_t)n * (((m + 7) & ~7) + 4);
     return need <= kSmallXlMaxFloats ? (int)need : 0;
 }
 
