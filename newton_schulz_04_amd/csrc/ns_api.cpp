@@ -305,10 +305,10 @@ void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* m
         d.xw = reinterpret_cast<float*>(ws + p.small_off[si]);
         std::memcpy(h + p.meta_small + si * sizeof(ns::SmallMat), &d, sizeof d);
     }
-    if (!p.syrk_tiles.empty())
-        std::memcpy(h + p.meta_syrk, p.syrk_tiles.data(), p.syrk_tiles.size() * sizeof(ns::Tile));
-    if (!p.poly_tiles.empty())
-        std::memcpy(h + p.meta_poly, p.poly_tiles.data(), p.poly_tiles.size() * sizeof(ns::Tile));
+    if (!p.syrk_run.empty())
+        std::memcpy(h + p.meta_syrk, p.syrk_run.data(), p.syrk_run.size() * sizeof(ns::Tile));
+    if (!p.poly_run.empty())
+        std::memcpy(h + p.meta_poly, p.poly_run.data(), p.poly_run.size() * sizeof(ns::Tile));
     if (!p.update_tiles.empty())
         std::memcpy(h + p.meta_update, p.update_tiles.data(), p.update_tiles.size() * sizeof(ns::Tile));
     std::memcpy(h + p.meta_part_prefix, p.part_prefix.data(), p.part_prefix.size() * sizeof(int32_t));
@@ -480,20 +480,30 @@ ns_status run(Context* c, const int64_t* shapes, const Layout& L, int32_t count,
     });
     if (e != hipSuccess)
         return hip_fail(e, "normalize kernel launch");
-    const int ns_ = (int)p.syrk_tiles.size(), nu = (int)p.update_tiles.size();
+    const int nu = (int)p.update_tiles.size();
+    // a symmetric stage: its whole tiles, then (when its last round is
+    // split) the half tiles, one timed launch pair
+    auto sym = [&](int stage, const ns::Tile* tl, int n, int split, int cur, int last, float ca, float cb,
+                   float cc) {
+        hipError_t r = ns::launch_gemm(dtype, stage, large, tl, n - split, cur, last, 0, ca, cb, cc, stream);
+        if (r == hipSuccess && split > 0)
+            r = ns::launch_gemm(dtype, stage, large, tl + (n - split), 2 * split, cur, last, 1, ca, cb, cc,
+                                stream);
+        return r;
+    };
     for (int s = 0; s < steps; ++s) {
         const int cur = s & 1, last = s == steps - 1;
         const float ca = coef(s, 0), cb = coef(s, 1), cc = coef(s, 2);
         e = timed(ns::kKindSyrk, stream, [&] {
-            return ns::launch_gemm(dtype, 0, large, syrk, ns_, cur, last, ca, cb, cc, stream);
+            return sym(0, syrk, (int)p.syrk_tiles.size(), p.syrk_split, cur, last, ca, cb, cc);
         });
         if (e == hipSuccess)
             e = timed(ns::kKindPoly, stream, [&] {
-                return ns::launch_gemm(dtype, 1, large, poly, ns_, cur, last, ca, cb, cc, stream);
+                return sym(1, poly, (int)p.poly_tiles.size(), p.poly_split, cur, last, ca, cb, cc);
             });
         if (e == hipSuccess)
             e = timed(ns::kKindUpdate, stream, [&] {
-                return ns::launch_gemm(dtype, 2, large, upd, nu, cur, last, ca, cb, cc, stream);
+                return ns::launch_gemm(dtype, 2, large, upd, nu, cur, last, 0, ca, cb, cc, stream);
             });
         if (e != hipSuccess)
             return hip_fail(e, "GEMM kernel launch");

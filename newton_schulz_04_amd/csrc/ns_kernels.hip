@@ -730,14 +730,19 @@ __device__ __forceinline__ char* tile_at(char* slot, int R, int x)
 // Whole-tile copy from the LDS tile to global rows of 256 bf16 at a pitch of
 // ld elements. Wavefront w moves rows 64w .. 64w + 63 (its slot `ws`), two
 // per instruction (lanes 0-31 and 32-63), lane p = l & 31 taking stored chunk p.
-__device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld, int wave, int lane)
+// own >= 0: only the columns of 64-column pieces own and own + 2 (a half
+// tile's), i.e. logical chunks c with (c >> 3) & 1 == own.
+__device__ __forceinline__ void tile_store(const char* ws, bf16* dst, int64_t ld, int wave, int lane,
+                                           int own = -1)
 {
     const int half = lane >> 5, p = lane & 31;
 #pragma unroll 4
     for (int q = 0; q < 32; ++q) {
         const int R = wave * 64 + 2 * q + half;
+        const int c = p ^ (R & 31);
         const uint4 v = *reinterpret_cast<const uint4*>(ws + (2 * q + half) * 512 + p * 16);
-        st16(dst + R * ld + 8 * (p ^ (R & 31)), v);
+        if (own < 0 || ((c >> 3) & 1) == own)
+            st16(dst + R * ld + 8 * c, v);
     }
 }
 
@@ -799,8 +804,9 @@ __device__ __forceinline__ void tile_store_user(const char* ws, bf16* user, void
 // an even lane keeps rows r0, r0+1 (d.x) for columns c, c+1, an odd lane
 // rows r0+2, r0+3 (d.y) for columns c-1, c. v_perm_b32 picks the 16-bit
 // halves (bytes 0..3 = the kept dword, 4..7 = the received one).
-__device__ __forceinline__ void write_tile_by_rows(char* rs0, char* rs1, const uint2 (&hv)[4][4][4], int wr,
-                                                   int wc, int fr, int fg)
+template <int NJ>
+__device__ __forceinline__ void write_tile_by_rows(char* rs0, char* rs1, const uint2 (&hv)[4][NJ][4], int wr,
+                                                   int wc, int fr, int fg, int jbase = 0)
 {
     const uint32_t odd = fr & 1;
     const uint32_t keep_y = 0u - odd;
@@ -810,10 +816,10 @@ __device__ __forceinline__ void write_tile_by_rows(char* rs0, char* rs1, const u
     for (int i = 0; i < 4; ++i) {
         char* rslot = i < 2 ? rs0 : rs1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int c = wc * 128 + j * 32 + fr;
+                const int c = wc * 128 + (jbase + j) * 32 + fr;
                 const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
                 const uint2 d = hv[i][j][rg];   // x: rows r0, r0+1; y: rows r0+2, r0+3
                 const uint32_t mine = (d.y & keep_y) | (d.x & ~keep_y);
@@ -965,7 +971,7 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
     if (LAST) {
         if (by_rows) {
             // (the barrier above: every wavefront has read its X_lo)
-            write_tile_by_rows(wr ? sl2 : sl0, wr ? sl3 : sl1, hv, wr, wc, fr, fg);
+            write_tile_by_rows<4>(wr ? sl2 : sl0, wr ? sl3 : sl1, hv, wr, wc, fr, fg);
             NS_WAIT_LDS_BARRIER();
             tile_store_user(ws, user, M.rows_tab, M.cols, gbi, M.m, gbj, M.n, wave, lane);
         } else {
@@ -990,11 +996,17 @@ __device__ __forceinline__ void update_epilogue_bf16(const LargeMat& M, char* sl
 // and pass 2 is not needed. The diagonal keeps its bf16 rounding residue
 // (d_i = v_ii - bf16(v_ii)), and for B the first-order terms of A's residue:
 // B_ij = (b + c (dA_i + dA_j)) A_ij + c (A A)_ij, plus b dA_i on the diagonal.
-template <int STAGE>
+// NJ == 2: a half tile (never diagonal); its wavefront blocks j are
+// 2 hsel + (0, 1), so all its columns of pass 1 lie in one slot per
+// wavefront (2 wc + hsel) and block (bj, bi) is stored by the two
+// wavefronts whose own slot that is; block (bi, bj) keeps only its columns.
+template <int STAGE, int NJ>
 __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, char* s1, char* s2, char* s3,
-                                                  f32x16 (&acc)[4][4], int64_t gbi, int64_t gbj, bool diag,
-                                                  float cb, float cc, int wave, int lane)
+                                                  f32x16 (&acc)[4][NJ], int64_t gbi, int64_t gbj, bool diag,
+                                                  float cb, float cc, int wave, int lane, int hsel)
 {
+    constexpr bool kHalf = NJ == 2;
+    const int jbase = kHalf ? 2 * hsel : 0;
     const int64_t ld = M.ldt;
     const int fr = lane & 31, fg = lane >> 5;
     const int wr = wave >> 1, wc = wave & 1;
@@ -1002,8 +1014,8 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
     float* dout = STAGE == 0 ? M.adiag : M.bdiag;
     char* ws = wave < 2 ? (wave == 0 ? s0 : s1) : (wave == 2 ? s2 : s3);
     // pass 1: tile column c lives in slot c >> 6 = 2 wc + (j >> 1)
-    char* cs0 = wc ? s2 : s0;
-    char* cs1 = wc ? s3 : s1;
+    char* cs0 = kHalf ? (wc ? (hsel ? s3 : s2) : (hsel ? s1 : s0)) : (wc ? s2 : s0);
+    char* cs1 = kHalf ? cs0 : (wc ? s3 : s1);
     // pass 2 (and the mirrored writes of a diagonal tile): tile row r lives
     // in slot r >> 6 = 2 wr + (i >> 1)
     char* rs0 = wr ? s2 : s0;
@@ -1011,12 +1023,12 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
 
     // A's diagonal residues at this lane's rows and columns, all requested
     // at once (they cross the barrier below in flight)
-    float dcol[4] = {0.f, 0.f, 0.f, 0.f};
+    float dcol[NJ] = {};
     f32x4 drows[4][4];
     if constexpr (STAGE == 1) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dcol[j] = gbl(M.adiag)[gbj + wc * 128 + j * 32 + fr];
+        for (int j = 0; j < NJ; ++j)
+            dcol[j] = gbl(M.adiag)[gbj + wc * 128 + (jbase + j) * 32 + fr];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1033,20 +1045,20 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
         const f32x4 (&drow)[4] = drows[i];
         // (A's 16 reads of a block row go out together, ahead of the writes
         // that the compiler cannot tell apart from them)
-        bf16x4 as[4][4];
+        bf16x4 as[NJ][4];
         if constexpr (STAGE == 1) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg)
-                    as[j][rg] = *reinterpret_cast<const bf16x4*>(
-                        tile_at(j < 2 ? cs0 : cs1, wc * 128 + j * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
+                    as[j][rg] = *reinterpret_cast<const bf16x4*>(tile_at(
+                        j < 2 ? cs0 : cs1, wc * 128 + (jbase + j) * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int c = wc * 128 + j * 32 + fr;
+                const int c = wc * 128 + (jbase + j) * 32 + fr;
                 const int r0 = wr * 128 + i * 32 + rg * 8 + fg * 4;
                 char* cslot = j < 2 ? cs0 : cs1;
                 bf16x4* loc = reinterpret_cast<bf16x4*>(tile_at(cslot, c, r0));
@@ -1062,7 +1074,7 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
                         v[e] = ce * (float)a[e] + cc * v[e];
                     }
                 }
-                if (!diag) {
+                if (kHalf || !diag) {
                     bf16x4 h;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -1091,34 +1103,42 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
     }
     NS_WAIT_LDS_BARRIER();
     // block (bj, bi): global row gbj + c, columns gbi ..
-    tile_store(ws, out + gbj * ld + gbi, ld, wave, lane);
-    if (diag)
+    if (!kHalf || (wave & 1) == hsel)
+        tile_store(ws, out + gbj * ld + gbi, ld, wave, lane);
+    if (!kHalf && diag)
         return;
 
     // this lane's bf16(v) back from the tile (rows r0..r0+3 of column c)
-    uint2 hv[4][4][4];
+    uint2 hv[4][NJ][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg)
-                hv[i][j][rg] = *reinterpret_cast<const uint2*>(
-                    tile_at(j < 2 ? cs0 : cs1, wc * 128 + j * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
+                hv[i][j][rg] = *reinterpret_cast<const uint2*>(tile_at(
+                    j < 2 ? cs0 : cs1, wc * 128 + (jbase + j) * 32 + fr, wr * 128 + i * 32 + rg * 8 + fg * 4));
     // pass 2 overwrites the tile: every wavefront's copy and reads are done
     NS_WAIT_LDS_BARRIER();
-    write_tile_by_rows(rs0, rs1, hv, wr, wc, fr, fg);
+    write_tile_by_rows<NJ>(rs0, rs1, hv, wr, wc, fr, fg, jbase);
     NS_WAIT_LDS_BARRIER();
     // block (bi, bj): global row gbi + r, columns gbj ..
-    tile_store(ws, out + gbi * ld + gbj, ld, wave, lane);
+    tile_store(ws, out + gbi * ld + gbj, ld, wave, lane, kHalf ? hsel : -1);
 }
 
-template <int DT, int STAGE, int LAST>
+// HALF (bf16 X X^T and bA + cA^2 only): the workgroup computes half of an
+// off-diagonal tile's columns, those in 64-column pieces 2 hsel and 2 hsel + 2
+// (wavefront column wc takes its 32-column blocks 2 hsel and 2 hsel + 1);
+// hsel is bit 30 of the tile's matrix index. Every element gets the same MFMA
+// sequence as in a whole tile, so the bits are the same; the half tiles of a
+// launch's last, partial round run on twice as many compute units.
+template <int DT, int STAGE, int LAST, int HALF>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
                                                       const Tile* __restrict__ tiles, int cur,
                                                       int last, float ca, float cb, float cc)
 {
     using OpT = typename Elt<DT>::type;
+    constexpr int NJ = HALF ? 2 : 4;   // 32-column blocks per wavefront
     // Four LDS slots (P then Q, 16 KB each), one object each: with the k loop
     // unrolled over the ring, every LDS read and every DMA names its slot
     // statically, so the compiler can see that a refill does not touch the
@@ -1133,7 +1153,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     __shared__ __attribute__((aligned(1024))) char lo3[2 * kSlotOpBytes];
 
     const Tile t = tiles[blockIdx.x];
-    const LargeMat& M = mats[t.mat];
+    const int hsel = HALF ? (int)((uint32_t)t.mat >> 30) : 0;
+    const int jbase = 2 * hsel;
+    const LargeMat& M = mats[HALF ? (t.mat & 0x3FFFFFFF) : t.mat];
     const char* P;
     const char* Q;
     // Operands read as k-rows (32 rows of 512 bytes per slot, see above)
@@ -1252,11 +1274,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
 
     const int fr = lane & 31, fg = lane >> 5;
     const int64_t gbi = (int64_t)t.bi * kTile, gbj = (int64_t)t.bj * kTile;
-    f32x16 acc[4][4];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.f;
@@ -1278,11 +1300,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             return (cl >> 5) * (32 * kSlotRowBytes) + kr * kSlotRowBytes + (((cl >> 3) & 3) << 4) + (cl & 7) * 2;
         return kr * kTrRowBytes + (((cl >> 3) ^ tr_swz(kr)) << 4) + (cl & 7) * 2;
     };
-    int aoff[4], boff[4];
+    int aoff[4], boff[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
         aoff[i] = kTP ? off_t(wr * 128 + i * 32) : lds_off(wr * 128 + i * 32 + fr, fg);
-        boff[i] = kSlotOpBytes + (kTQ ? off_t(wc * 128 + i * 32) : lds_off(wc * 128 + i * 32 + fr, fg));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int cb0 = wc * 128 + (jbase + j) * 32;
+        boff[j] = kSlotOpBytes + (kTQ ? off_t(cb0) : lds_off(cb0 + fr, fg));
     }
     constexpr int kTrStep = kPT ? 16 * kSlotRowBytes : 16 * kTrRowBytes;   // 16 k-rows
     constexpr int kTrHalf = kPT ? 4 * kSlotRowBytes : 4 * kTrRowBytes;     // 4 k-rows
@@ -1294,32 +1319,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         }
         return *reinterpret_cast<const uint4*>(sp + (off ^ (ks << 5)));
     };
-    auto read_frags = [&](const char* sp, int ks, uint4 (&af)[4], uint4 (&bfr)[4]) {
+    auto read_frags = [&](const char* sp, int ks, uint4 (&af)[4], uint4 (&bfr)[NJ]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             af[i] = read_frag(sp, aoff[i], ks, kTP);
-            bfr[i] = read_frag(sp, boff[i], ks, kTQ);
+            if (i < NJ)
+                bfr[i] = read_frag(sp, boff[i], ks, kTQ);
         }
     };
-    auto mfma_block = [&](const uint4 (&af)[4], const uint4 (&bfr)[4]) {
+    auto mfma_block = [&](const uint4 (&af)[4], const uint4 (&bfr)[NJ]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
                 Mfma<OpT>::mac(acc[i][j], af[i], bfr[j]);
     };
     auto interleave = []() __attribute__((always_inline)) {
-        // Per k-step: the 16 MFMAs with the LDS reads of the next k-step
-        // (8 transposed 8-byte reads or 4 16-byte reads per operand) and half
-        // of the refill's DMAs (4) spread between them. Issued in one burst,
-        // the DMAs stall the wavefront at issue while the memory pipeline is
-        // full, and that pipeline then runs dry during the MFMAs.
-        constexpr int nreads = (kTP ? 8 : 4) + (kTQ ? 8 : 4);
+        // Per k-step: the 4 NJ MFMAs with the LDS reads of the next k-step
+        // (8 transposed 8-byte reads or 4 16-byte reads per operand and 4
+        // blocks) and half of the refill's DMAs (4) spread between them.
+        // Issued in one burst, the DMAs stall the wavefront at issue while
+        // the memory pipeline is full, and that pipeline then runs dry during
+        // the MFMAs.
+        constexpr int nmf = 4 * NJ;
+        constexpr int nreads = (kTP ? 8 : 4) + (kTQ ? 2 : 1) * NJ;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            if (q % 4 == 0)
+        for (int q = 0; q < nmf; ++q) {
+            if (q % (nmf / 4) == 0)
                 __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-            if (q < nreads)
+            // whole tiles: one read per MFMA while reads last; half tiles
+            // (12 reads, 8 MFMAs): two per MFMA first, then one
+            const int nr = NJ == 4 ? (q < nreads ? 1 : 0) : (q < nreads - nmf ? 2 : 1);
+            if (nr >= 1)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (nr >= 2)
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
@@ -1353,7 +1386,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             rowscale[ii] = ca + gbl(M.bdiag)[gbi + wr * 128 + ii * 32 + fr];
     }
     // peel slot P, k-step ks of the slot
-    auto ident = [&](int P, int ks, const uint4 (&bfr)[4]) {
+    auto ident = [&](int P, int ks, const uint4 (&bfr)[NJ]) {
         const int ii = P & 3;
         // A fragment: lane l holds row l & 31, k = 8 (l >> 5) + e of the
         // 32 x 16 block; the identity sits at e = (l & 31) - 16 ks - 8 (l >> 5).
@@ -1374,7 +1407,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         const uint4 fh = make_uint4(wh[0], wh[1], wh[2], wh[3]);
         const uint4 fl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             Mfma<OpT>::mac(acc[ii][j], fh, bfr[j]);
             Mfma<OpT>::mac(acc[ii][j], fl, bfr[j]);
         }
@@ -1393,7 +1426,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         issue_blk_quarter(pre_blk, M.ldt, sp, quarter, wave, lane, q0, q1);
     };
 
-    uint4 fa[4], fb[4], ga[4], gb[4];
+    uint4 fa[4], fb[NJ], ga[4], gb[NJ];
     // H >= 0: slot sb + H of the bf16 update (adds a X_hi);
     // L >= 0: instead of a slot, load quarter L of the update's X_lo tile
     auto step = [&](const char* cur, char* refill, const char* next, int s, auto peel, auto lq) __attribute__((always_inline)) {
@@ -1492,12 +1525,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     // Epilogues. Lane l, block (i, j), register group rg holds rows
     // lr0..lr0+3 of column lc (tile-local).
     if constexpr (STAGE == 0 && IsBf16<OpT>::value) {
-        sym_epilogue_bf16<0>(M, sl0, sl1, sl2, sl3, acc, gbi, gbj, t.bi == t.bj, cb, cc, wave, lane);
+        sym_epilogue_bf16<0, NJ>(M, sl0, sl1, sl2, sl3, acc, gbi, gbj, !HALF && t.bi == t.bj, cb, cc, wave, lane,
+                                 hsel);
         return;
     } else if constexpr (STAGE == 1 && IsBf16<OpT>::value) {
-        sym_epilogue_bf16<1>(M, sl0, sl1, sl2, lo3, acc, gbi, gbj, t.bi == t.bj, cb, cc, wave, lane);
+        sym_epilogue_bf16<1, NJ>(M, sl0, sl1, sl2, lo3, acc, gbi, gbj, !HALF && t.bi == t.bj, cb, cc, wave, lane,
+                                 hsel);
         return;
     }
+    if constexpr (!HALF) {
     // fp32 path: the epilogues store straight from the accumulators (a
     // 256 x 256 fp32 tile does not fit the LDS), and there are no residues.
     if (STAGE == 0 || STAGE == 1) {
@@ -1630,27 +1666,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             }
         }
     }
+    }
 }
 
 template <typename OpT, int STAGE>
-hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, int cur, int last,
+hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, int cur, int last, int half,
                          float a, float b, float c, hipStream_t stream)
 {
     // The bf16 update's last step (it writes the caller's buffer) is its own
-    // instantiation, so the other steps' epilogue carries no code for it.
+    // instantiation, so the other steps' epilogue carries no code for it; so
+    // are the half tiles of the bf16 symmetric stages.
     constexpr int DT = IsBf16<OpT>::value ? 0 : 1;
     if constexpr (STAGE == 2 && DT == 0) {
         if (last) {
-            hipLaunchKernelGGL((k_gemm<DT, STAGE, 1>), dim3(ntiles), dim3(kThreads), 0, stream, mats,
+            hipLaunchKernelGGL((k_gemm<DT, STAGE, 1, 0>), dim3(ntiles), dim3(kThreads), 0, stream, mats,
                                tiles, cur, last, a, b, c);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((k_gemm<DT, STAGE, 0>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
+    if constexpr (STAGE < 2 && DT == 0) {
+        if (half) {
+            hipLaunchKernelGGL((k_gemm<DT, STAGE, 0, 1>), dim3(ntiles), dim3(kThreads), 0, stream, mats,
+                               tiles, cur, last, a, b, c);
+            return hipGetLastError();
+        }
+    }
+    if (half)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm<DT, STAGE, 0, 0>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
                        cur, last, a, b, c);
     return hipGetLastError();
 }
-
 }  // namespace
 
 int small_lds_floats(int max_xl_floats)
@@ -1730,16 +1776,16 @@ hipError_t launch_scale_out(int dtype, const LargeMat* mats, int nmats, const in
 }
 
 hipError_t launch_gemm(int dtype, int stage, const LargeMat* mats, const Tile* tiles, int ntiles,
-                       int cur, int last, float a, float b, float c, hipStream_t stream)
+                       int cur, int last, int half, float a, float b, float c, hipStream_t stream)
 {
     if (dtype == 0) {
-        if (stage == 0) return launch_gemm_t<bf16, 0>(mats, tiles, ntiles, cur, last, a, b, c, stream);
-        if (stage == 1) return launch_gemm_t<bf16, 1>(mats, tiles, ntiles, cur, last, a, b, c, stream);
-        return launch_gemm_t<bf16, 2>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+        if (stage == 0) return launch_gemm_t<bf16, 0>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
+        if (stage == 1) return launch_gemm_t<bf16, 1>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
+        return launch_gemm_t<bf16, 2>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
     }
-    if (stage == 0) return launch_gemm_t<float, 0>(mats, tiles, ntiles, cur, last, a, b, c, stream);
-    if (stage == 1) return launch_gemm_t<float, 1>(mats, tiles, ntiles, cur, last, a, b, c, stream);
-    return launch_gemm_t<float, 2>(mats, tiles, ntiles, cur, last, a, b, c, stream);
+    if (stage == 0) return launch_gemm_t<float, 0>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
+    if (stage == 1) return launch_gemm_t<float, 1>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
+    return launch_gemm_t<float, 2>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
 }
 
 }  // namespace ns

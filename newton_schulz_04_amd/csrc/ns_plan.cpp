@@ -103,6 +103,61 @@ std::vector<Tile> order_tiles(const Plan& p, int stage)
     return out;
 }
 
+// Compute units of the device the tile lists are cut for (MI355X).
+constexpr size_t kCus = 256;
+
+// The last r = n mod kCus tiles of a symmetric stage form a partial last
+// round. When r <= kCus / 2 (after at least one full round), they run as
+// 2r half tiles (each half of a tile's columns, the same bits) on twice as
+// many compute units. Diagonal tiles cannot be halved: those in the tail
+// trade places with an off-diagonal tile of the same matrix before it
+// (same K depth, same XCD position where there is one). Returns r, or 0 when
+// nothing is split.
+int32_t split_tail(std::vector<Tile>& tl)
+{
+    const size_t n = tl.size(), r = n % kCus;
+    if (n <= kCus || r == 0 || r > kCus / 2)
+        return 0;
+    const size_t t0 = n - r;
+    for (size_t pos = t0; pos < n; ++pos) {
+        if (tl[pos].bi != tl[pos].bj)
+            continue;
+        size_t found = SIZE_MAX;
+        for (int pass = 0; pass < 2 && found == SIZE_MAX; ++pass)
+            for (size_t q = t0; q-- > 0;)
+                if (tl[q].mat == tl[pos].mat && tl[q].bi != tl[q].bj &&
+                    (pass == 1 || q % kXcds == pos % kXcds)) {
+                    found = q;
+                    break;
+                }
+        if (found == SIZE_MAX)
+            return 0;
+        std::swap(tl[pos], tl[found]);
+    }
+    return (int32_t)r;
+}
+
+// The uploaded list: tiles [0, n - r), then the halves of the last r. Tiles
+// k and k' of a group of 8 sat on XCD k mod 8; their halves go to positions
+// 16 g + k mod 8 and 16 g + c + k mod 8 of the half launch (c = the group's
+// size), i.e. the same XCD for whole groups, so two halves share their
+// operand blocks in one L2.
+std::vector<Tile> run_list(const std::vector<Tile>& tl, int32_t split)
+{
+    const size_t n = tl.size(), r = (size_t)split, t0 = n - r;
+    std::vector<Tile> out(tl.begin(), tl.begin() + t0);
+    out.resize(n + r);
+    for (size_t g = 0; g * kXcds < r; ++g) {
+        const size_t c = std::min((size_t)kXcds, r - g * kXcds);
+        for (size_t j = 0; j < c; ++j) {
+            const Tile t = tl[t0 + g * kXcds + j];
+            out[t0 + 2 * g * kXcds + j] = Tile{t.mat, t.bi, t.bj};
+            out[t0 + 2 * g * kXcds + c + j] = Tile{(int32_t)((uint32_t)t.mat | (1u << 30)), t.bi, t.bj};
+        }
+    }
+    return out;
+}
+
 }  // namespace
 
 int64_t ns_cost(int64_t rows, int64_t cols)
@@ -201,6 +256,12 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
     p.syrk_tiles = order_tiles(p, kStageSyrk);
     p.poly_tiles = order_tiles(p, kStagePoly);
     p.update_tiles = order_tiles(p, kStageUpdate);
+    if (dtype == 0) {
+        p.syrk_split = split_tail(p.syrk_tiles);
+        p.poly_split = split_tail(p.poly_tiles);
+    }
+    p.syrk_run = run_list(p.syrk_tiles, p.syrk_split);
+    p.poly_run = run_list(p.poly_tiles, p.poly_split);
     p.total_parts = p.part_prefix.back();
     p.total_prep = p.prep_prefix.back();
 
@@ -255,9 +316,9 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
     p.meta_small = off;
     off = align_up(off + sizeof(SmallMat) * p.small.size());
     p.meta_syrk = off;
-    off = align_up(off + sizeof(Tile) * p.syrk_tiles.size());
+    off = align_up(off + sizeof(Tile) * p.syrk_run.size());
     p.meta_poly = off;
-    off = align_up(off + sizeof(Tile) * p.poly_tiles.size());
+    off = align_up(off + sizeof(Tile) * p.poly_run.size());
     p.meta_update = off;
     off = align_up(off + sizeof(Tile) * p.update_tiles.size());
     p.meta_part_prefix = off;

@@ -51,10 +51,13 @@ def source_hash():
 
 def kernel_kind(name):
     """Short name of a kernel from its (demangled or mangled) name."""
-    m = (re.search(r"k_gemm<\s*\d+\s*,\s*(\d+)\s*(?:,\s*\d+\s*)?>", name) or
-         re.search(r"k_gemmI(?:Li\d+E|DF16b|f)Li(\d+)E", name))
+    # k_gemm<dtype, stage, last, half>: half tiles of a split last round
+    # are their own kind (<stage>_half)
+    m = (re.search(r"k_gemm<\s*\d+\s*,\s*(\d+)\s*(?:,\s*\d+\s*)?(?:,\s*(\d+)\s*)?>", name) or
+         re.search(r"k_gemmI(?:Li\d+E|DF16b|f)Li(\d+)E(?:Li\d+E)?(?:Li(\d+)E)?", name))
     if m:
-        return GEMM_KINDS.get(m.group(1), "gemm" + m.group(1))
+        kind = GEMM_KINDS.get(m.group(1), "gemm" + m.group(1))
+        return kind + "_half" if m.group(2) == "1" else kind
     for short in ("k_norm_partial", "k_norm_final", "k_prep", "k_small", "k_scale_out"):
         if short in name:
             return short[2:]
@@ -189,6 +192,12 @@ def summary_md(stats_csv, traffic_json, bench_json, title, shapes, kt_command, m
         e = t["kernels"].get(k)
         if not e:
             continue
+        # a split last round's half tiles are a second launch of the stage
+        # (one per step, like the main launch): their bytes count with it
+        h = t["kernels"].get(k + "_half")
+        if h:
+            e = {"fetch_bytes": e["fetch_bytes"] + h["fetch_bytes"],
+                 "write_bytes": e["write_bytes"] + h["write_bytes"]}
         rate = ""
         if ks.get(k):
             rate = f"{(e['fetch_bytes'] + e['write_bytes']) / (ks[k] * 1e-3) / 1e12:.2f} TB/s"
@@ -212,9 +221,11 @@ twice the MFMA work they do.
     return f"""# {title}
 
 One bench step = one `ns_orthogonalize_batched` call over the batch: norm_partial,
-norm_final, prep, then 5 x (syrk = `k_gemm<0, 0, 0>` X X^T, poly = `k_gemm<0, 1, 0>`
-bA + cA^2, update = `k_gemm<0, 2, 0>` aX + BX; the fifth update is `k_gemm<0, 2, 1>`,
-which writes the caller's buffer). `copy_probe` rows are the runtime's
+norm_final, prep, then 5 x (syrk = `k_gemm<0, 0, 0, 0>` X X^T, poly = `k_gemm<0, 1, 0, 0>`
+bA + cA^2, update = `k_gemm<0, 2, 0, 0>` aX + BX; the fifth update is `k_gemm<0, 2, 1, 0>`,
+which writes the caller's buffer; syrk_half and poly_half = `k_gemm<0, 0|1, 0, 1>`
+run the half tiles of a split last round, a second launch of the stage, and
+count with it in the traffic table). `copy_probe` rows are the runtime's
 device copies (bench restores its inputs between steps, outside the timed region).
 Run from the repository root with `export TMPDIR=/tmp` and the library built
 in-tree (`python -c "import __graft_entry__ as g; g.build()"`).
