@@ -144,6 +144,24 @@ def test_tiles_cover_each_block_once(shapes):
             assert {k for k in seen if k[0] == i} == want
 
 
+@pytest.mark.parametrize("count", [1, 7, 8, 12])
+def test_split_tail_is_off_diagonal(count):
+    # A symmetric stage whose last round is partial (r = n mod 256 tiles,
+    # r <= 128, after a full round) runs those r tiles as half tiles, which
+    # exist only for off-diagonal tiles: the planner moves diagonal tiles out
+    # of the tail. 8192x6144: 300 upper tiles per matrix, 24 of them diagonal.
+    shapes = [(8192, 6144)] * count
+    for stage in (0, 1):
+        tiles, _ = ns.plan_tiles(shapes, ns.NS_BF16, stage)
+        n = len(tiles)
+        assert n == 300 * count
+        r = n % 256
+        assert n > 256 and 0 < r <= 128
+        assert all(bi != bj for _, bi, bj, _ in tiles[n - r:])
+        # still every upper tile once
+        assert len({(m, bi, bj) for m, bi, bj, _ in tiles}) == n
+
+
 def _makespan(costs, workers):
     """Greedy list schedule in list order (the dispatcher's behaviour)."""
     import heapq
