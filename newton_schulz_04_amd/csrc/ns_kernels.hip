@@ -1256,6 +1256,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     constexpr bool kPre = kIdent || (STAGE == 1 && IsBf16<OpT>::value);
     const int sb = kIdent ? t.bi * 8 : 0;
     const int soff_end = range_p > range_q ? range_p : range_q;
+    // X X^T half tiles read only the 4 Q panels their columns lie in
+    // (2 hsel, 2 hsel + 1, 2 hsel + 4, 2 hsel + 5: instructions q = hsel and
+    // q = hsel + 2), 6 DMAs per wavefront and slot instead of 8 (3 in each
+    // half of a step), which the wait counts below follow.
+    constexpr bool kHalfQ = HALF && kPT;
     auto issue = [&](char* sp, int s, int q0 = 0, int q1 = 4) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = q0; q < q1; ++q) {
@@ -1266,9 +1271,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rp, (lds_ptr_t)(sp + (wave + 4 * q) * 1024), 16, voff_p, kPT ? soff_pt : kTP ? soff_t : soff_n,
                 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rq, (lds_ptr_t)(sp + kSlotOpBytes + (wave + 4 * q) * 1024), 16, voff_q,
-                kPT ? soff_pt : kPQ ? soff_pq : kTQ ? soff_t : soff_n, 0, 0);
+            if (!kHalfQ || (q & 1) == hsel)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rq, (lds_ptr_t)(sp + kSlotOpBytes + (wave + 4 * q) * 1024), 16, voff_q,
+                    kPT ? soff_pt : kPQ ? soff_pq : kTQ ? soff_t : soff_n, 0, 0);
         }
     };
 
@@ -1441,7 +1447,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
         interleave();
         if constexpr (H >= 0) ident(H, 0, fb);
         // slot s + 1 complete: younger are slot s + 2 and half of s + 3
-        asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if constexpr (kHalfQ)
+            asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if constexpr (L >= 0)
             issue_lo(refill, L, 4, 8);
         else
@@ -1483,6 +1492,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     issue(sl2, 2);
     if constexpr (kPre)
         asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    else if constexpr (kHalfQ)
+        asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
     else
         asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
     read_frags(sl0, 0, fa, fb);
