@@ -26,6 +26,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "ns_kernels.h"
 
 namespace ns {
@@ -1726,15 +1730,25 @@ hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
                         const CoeffTable& coeffs, int xl_floats, hipStream_t stream)
 {
     const size_t lds = sizeof(float) * (size_t)small_lds_floats(xl_floats);
-    static bool attr[2] = {false, false};
-    if (!attr[dtype]) {
-        const size_t max_lds = sizeof(float) * (size_t)small_lds_floats(kSmallXlMaxFloats);
-        const hipError_t e = dtype == 0
-            ? hipFuncSetAttribute((const void*)k_small<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds)
-            : hipFuncSetAttribute((const void*)k_small<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
-        if (e != hipSuccess)
-            return e;
-        attr[dtype] = true;
+    // Allow the kernel its largest dynamic LDS once per device and dtype
+    // (above the 64 KB default).
+    static std::mutex mu;
+    static std::set<std::pair<int, int>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (!done.count({dev, dtype})) {
+            const int max_lds = (int)(sizeof(float) * (size_t)small_lds_floats(kSmallXlMaxFloats));
+            e = dtype == 0
+                ? hipFuncSetAttribute((const void*)k_small<0>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds)
+                : hipFuncSetAttribute((const void*)k_small<1>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+            if (e != hipSuccess)
+                return e;
+            done.insert({dev, dtype});
+        }
     }
     if (dtype == 0)
         hipLaunchKernelGGL(k_small<0>, dim3(count), dim3(kSmallThreads), lds, stream, mats, steps, coeffs, xl_floats);
