@@ -252,6 +252,25 @@ def test_small_large_boundary(dtype, shape):
     assert rel_err(y, oracle_run(g)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(24, 1024), (24, 1025), (1025, 24), (32, 796), (32, 797), (5, 2389),
+                                   (5, 4000)])
+def test_small_path_resident_and_streamed(dtype, shape):
+    # The fused small-matrix kernel keeps X in LDS while n x (m rounded up to
+    # 8, plus 4) floats fit 28672 (24 x 1024, 32 x 796 and 5 x 2389 are the
+    # largest such), else streams it from an L2-resident buffer in 128-column
+    # chunks (24 x 1025, 32 x 797, 5 x 4000; ragged last chunks). Both paths,
+    # alone and in one batch, against the oracle; a matrix's path and bits do
+    # not depend on the batch.
+    g = workloads.gaussian(shape, seed=43, index=shape[0] * 7 + shape[1], dtype=dtype)
+    (y,) = gpu_run([g])
+    assert rel_err(y, oracle_run(g)) <= TOL[dtype]
+    other = workloads.gaussian((16, 300), seed=43, index=1, dtype=dtype)
+    y2, _ = gpu_run([g, other])
+    assert torch.equal(y.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       y2.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
 @pytest.mark.parametrize("shape", [(520, 300), (300, 520)])
 def test_unaligned_base_pointer(shape):
     # a matrix starting 2 bytes past a 16-byte boundary takes the element-wise
