@@ -8,7 +8,9 @@
 //   small matrices : k_small (one launch for all of them)
 //   large matrices : norm pieces, norm fold, normalize/transpose/pad, then per
 //                    step the three grouped GEMM stages X X^T, bA + cA^2,
-//                    aX + BX (the last one writes the caller's buffers).
+//                    aX + BX (the last one writes the caller's buffers); a
+//                    bf16 symmetric stage whose last round is split runs its
+//                    half tiles as a second launch.
 //
 // Nothing here waits for the device. Workspace growth uses stream-ordered
 // allocation (hipMallocAsync / hipFreeAsync); metadata goes up from pinned

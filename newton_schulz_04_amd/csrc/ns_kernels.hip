@@ -5,19 +5,23 @@
 // then `steps` times A = X X^T, B = bA + cA^2, X = aX + BX.
 //
 // Kernels:
-//   k_small        whole iteration for min(rows, cols) <= 32, one workgroup per
-//                  matrix, fp32 arithmetic, X kept in an L2-resident buffer.
+//   k_small        whole iteration for min(rows, cols) <= 32, one workgroup of
+//                  512 threads per matrix, fp32 arithmetic, X resident in LDS
+//                  when it fits, else streamed from an L2-resident buffer.
 //   k_norm_partial sum of squares of a 16K-element piece of G (wave shuffles).
 //   k_norm_final   folds the pieces of a matrix in fixed order -> 1/(||G||+eps).
 //   k_prep         X = G/(||G||+eps), transposed when rows > cols, zero-padded
-//                  to multiples of 256; writes X^T (bf16: X_hi = bf16(X) and
-//                  X_lo = bf16(X - X_hi); fp32: X^T and X) through a 64x64 LDS
-//                  tile.
-//   k_gemm<stage>  grouped 256x256 MFMA GEMM over a tile list, C = P Q^T with
-//                  both operands K-contiguous in memory:
+//                  to multiples of 256; writes X^T (bf16: X_hi = bf16(X) in
+//                  column panels of 32 and X_lo = bf16(X - X_hi) row-major;
+//                  fp32: X^T and X), through a 64x64 LDS tile where it must
+//                  transpose.
+//   k_gemm<dtype, stage, last, half>
+//                  grouped 256x256 MFMA GEMM over a tile list, C = P Q^T:
 //                    stage 0  P = Q = X            -> A (upper tiles, mirrored)
 //                    stage 1  P = Q = A (= A^T)    -> B = bA + cA^2 (mirrored)
 //                    stage 2  P = B, Q = X^T store -> X = aX + BX
+//                  last: the final update writes the caller's buffer; half:
+//                  the half tiles of a symmetric stage's split last round.
 //   k_scale_out    steps == 0: G <- G/(||G||+eps).
 //
 // Every sum has a fixed order that does not depend on the batch, on the
@@ -633,10 +637,14 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM, C = P Q^T on a 256x256 tile, both operands row-major with K
-// contiguous and leading dimension K. One workgroup of 4 wavefronts (2 x 2),
+// Grouped GEMM, C = P Q^T on a 256x256 tile, in general both operands
+// row-major with K contiguous (bf16 operands are also read as k-rows or from
+// X_hi's column panels, see k_gemm). One workgroup of 4 wavefronts (2 x 2),
 // each wavefront 128x128 = 4x4 MFMA blocks of 32x32 (16 fp32 accumulators
-// per lane per block).
+// per lane per block). The tile is as large as the accumulators allow (the
+// 256 AGPRs of each lane), and it sets what the kernels cost: 32 KB of
+// operands per 32-deep slot, streamed from L2 at ~12 TB/s over the chip,
+// whose power is what lowers the shader clock under these kernels.
 //
 // K advances in slots of 64 bytes per row (32 bf16 / 16 fp32): one slot of
 // one operand is 256 rows x 64 B = 16 KB, and P and Q slots go through a ring
