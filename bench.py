@@ -9,6 +9,7 @@ normalize/transpose, 5 x (X X^T, bA + cA^2, aX + BX), write-back.
 
 Workloads: dense_lowrank (default), ragged_remainder_R (R of the remainder
 pool's 8192x6144 matrices, the last one passed through 64 row shards),
+dense_lowrank_fp32 (the default's matrices through the fp32 path, fp32 MFMA),
 moe_mixed (130 matrices of four shapes), attn_gate (32 x 18x2304 passed as 8
 padded row shards each) and tiny_fp32 (4 x 64x32 fp32). The last two run in
 the fused small-matrix kernel: fp32 arithmetic on the vector ALUs, reported
@@ -31,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "NS-orthogonalized matrices/s + TFLOP/s (% bf16 MFMA peak), 8192x6144 bf16"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector (the fused small-matrix kernel)
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 MFMA (the fp32 tiled path)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -45,6 +47,11 @@ def make_workload(name):
         mats = [wl.dense_lowrank_matrix(i) for i in range(wl.DENSE_COUNT)]
         desc = {"workload": "dense_lowrank", "matrices": 8, "shape": [8192, 6144],
                 "dtype": "bf16", "input": "rank-64 L@R + 1e-3*N(0,1), seed 2", "ns_steps": 5}
+    elif name == "dense_lowrank_fp32":
+        # the same matrices (their bf16 values, exactly) through the fp32 path
+        mats = [wl.dense_lowrank_matrix(i).float() for i in range(wl.DENSE_COUNT)]
+        desc = {"workload": "dense_lowrank_fp32", "matrices": 8, "shape": [8192, 6144],
+                "dtype": "fp32", "input": "rank-64 L@R + 1e-3*N(0,1), seed 2, as fp32", "ns_steps": 5}
     elif name.startswith("ragged_remainder_"):
         r = int(name.rsplit("_", 1)[1])
         mats = [c.mat for c in wl.ragged_remainder(r, world=64, padded=True)]
@@ -178,6 +185,7 @@ def main():
     real = tuple(desc.get("real_shape", ())) or None
     flops_batch = sum(wl.flops_per_matrix(*(real or (r, c))) for r, c in shapes)
     small_batch = all(min(r, c) <= 32 for r, c in shapes)
+    fp32 = all(m.dtype == torch.float32 for m in mats)
     cpu_mats = [m.clone() for m in mats] if small_batch else None
     pristine = [m.cuda() for m in mats]
     del mats
@@ -229,9 +237,10 @@ def main():
     else:
         dom = max((k for k in kernels if k in per_kind), key=lambda k: kernels[k]["ms_total"])
         achieved = per_kind[dom] / (kernels[dom]["ms_avg"] * 1e-3) / 1e12
+        peak = PEAK_FP32_MFMA_TFLOPS if fp32 else PEAK_BF16_TFLOPS
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4),
                     "traffic": measured_traffic(args.workload, dom)}
     ms_per_step = elapsed / args.steps * 1e3
     tflops = flops_batch / (elapsed / args.steps) / 1e12
@@ -247,7 +256,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if small_batch else "bf16",
+        "dtype": "f32" if small_batch or fp32 else "bf16",
         "data": "synthetic",
         "config": desc,
         "tflops": round(tflops, 1),
