@@ -3,9 +3,7 @@
  * MI355X (gfx950).
  *
  * The operation. Each matrix G (rows x cols, row-major) of a batch is replaced
- * in place by its Newton-Schulz orthogonalization, Muon's quintic iteration
- * (K. Jordan et al., "Muon: An optimizer for hidden layers in neural
- * networks", 2024):
+ * in place by its Newton-Schulz orthogonalization:
  *
  *     X = G / (||G||_F + 1e-7)
  *     if rows > cols: X = X^T                    (X is m x n, m <= n)
@@ -18,15 +16,32 @@
  * FSDP2 shards", Fix section, which also states that zero rows stay zero) and
  * rank its cost as max(M,N)*min(M,N)^2 (NVIDIA/Megatron-LM PR #6379, "Balance
  * LayerWise optimizer shards by Newton-Schulz cost, not parameter size",
- * Changes item 1). They do not give the coefficients; (a, b, c) =
- * (3.4445, -4.7750, 2.0315) with 5 steps is the usual choice and what
+ * Changes item 1). They give neither the iteration's coefficients nor its
+ * normalization; the specification this library implements fixes them: the
+ * Frobenius normalization with eps = 1e-7 added to the norm, the orientation
+ * rows <= cols, 5 steps and (a, b, c) = (3.4445, -4.7750, 2.0315), which
  * NS_QUINTIC_* below hold.
  *
- * Precision. bf16 matrices: products on bf16 MFMA with fp32 accumulation, an
- * fp32 master copy of X carried between steps, result rounded to bf16
- * (round-to-nearest-even); matrices with min(rows, cols) <= 32 run the whole
- * iteration in fp32. fp32 matrices: fp32 arithmetic throughout.
- * Zero rows and columns of G come back as exact +0.0.
+ * Precision (what the result is computed with, not a promise of bits):
+ *  - bf16 matrices with min(rows, cols) > 32: products on bf16 MFMA with fp32
+ *    accumulation. X is carried between steps as two bf16 arrays,
+ *    X_hi = bf16(X) and X_lo = bf16(X - X_hi), about 17 significant bits; A
+ *    and B are stored as bf16 operands (the same bf16 A in b A and in A^2),
+ *    with the rounding residues of their diagonals kept in fp32 and added
+ *    back (first-order terms in B, the diagonal of B in the update). The
+ *    result is rounded to bf16 (round-to-nearest-even). Relative Frobenius
+ *    error against an fp64 evaluation of the same iteration: a few 1e-3 on
+ *    the shapes tested, within 2e-2.
+ *  - bf16 matrices with min(rows, cols) <= 32: the whole iteration in fp32
+ *    on the vector units, result rounded to bf16.
+ *  - fp32 matrices: fp32 arithmetic throughout (fp32 MFMA for the tiled
+ *    path), within 1e-4 of the fp64 evaluation.
+ *  - The norm sums squares in fp32 with per-piece power-of-two scaling, so
+ *    every finite input normalizes (entries up to FLT_MAX); an Inf or NaN
+ *    entry propagates (see ns_orthogonalize_batched).
+ * Zero rows and columns of G come back as exact +0.0, and a matrix gives the
+ * same bits alone, in any batch, at any position and with trailing zero rows
+ * appended.
  *
  * Threading. Entry points may be called from several host threads; calls
  * that share a (device, stream) pair are serialized on a lock. All GPU work
@@ -81,14 +96,37 @@ typedef enum {
  *           stream order. Host arrays are only read before the call returns.
  *
  * Workspace: the library keeps a device workspace per (device, stream) pair,
- * grown on demand with stream-ordered allocation, plus a small cache of batch
- * plans keyed by the argument values. Two calls on the same stream are
- * ordered by the stream; calls on different streams use separate workspaces.
+ * grown on demand with stream-ordered allocation (hipMallocAsync /
+ * hipFreeAsync), plus a cache of up to 64 batch plans keyed by the argument
+ * values (shapes, pointers, dtype). Two calls on the same stream are ordered
+ * by the stream; calls on different streams use separate workspaces.
  *
- * Errors: NS_EINVAL (negative count/steps/shape, NULL ptrs/shapes with
- * count > 0, NULL pointer for a non-empty matrix, NULL coeffs with steps > 0,
- * a dimension above 2^24), NS_EDTYPE, NS_ENOMEM, NS_EHIP. On any error the
- * message is available from ns_last_error(). NaN and Inf propagate unchecked.
+ * Never blocks: the call enqueues its work and returns without waiting for
+ * the device, however much work is already queued on the stream (the hang
+ * and hidden sync point microsoft/dion PR #74, "Fix
+ * megabatch_orthogonalize_async hang on empty FSDP2 shards", Concrete repro
+ * and review thread, are about). A batch not in the plan cache uploads its
+ * descriptors and tile lists from pinned host staging buffers; one still
+ * feeding an earlier upload is never waited for: a new buffer is allocated
+ * instead, up to 256 MiB of them per (device, stream), past which the call
+ * returns NS_ENOMEM (with nothing enqueued) rather than wait.
+ *
+ * Errors (all reported before anything is enqueued, except NS_EHIP):
+ *   NS_EINVAL  negative count, steps or dimension; NULL ptrs/shapes with
+ *              count > 0; NULL pointer for a non-empty matrix; a pointer not
+ *              aligned to the element size; NULL coeffs with steps > 0; a
+ *              dimension above 2^24; a tiled-path matrix (min(rows, cols) >
+ *              32) whose padded operand is too large for 32-bit buffer
+ *              offsets: with m, n rounded up to multiples of 256 (mp, np),
+ *              np x mp x element size must stay below 2 GiB and
+ *              np x 256 x element size below 2 GiB (e.g. 32768 x 32768 bf16
+ *              or 8192 x 131072 bf16 is rejected; 10240 x 10240 and
+ *              8192 x 65536 bf16 are accepted).
+ *   NS_EDTYPE  unknown dtype.
+ *   NS_ENOMEM  the workspace or the metadata staging cannot be allocated.
+ *   NS_EHIP    a HIP call or kernel launch failed.
+ * On any error the message is available from ns_last_error(). NaN and Inf
+ * propagate unchecked: a NaN entry makes the whole result NaN.
  */
 ns_status ns_orthogonalize_batched(void* const* ptrs, const int64_t* shapes,
                                    int32_t count, int32_t steps,
@@ -190,21 +228,26 @@ ns_status ns_plan_ranks(const int64_t* numel, const int64_t* cost, int32_t count
 
 /*
  * Device workspace bytes a call with these shapes and dtype needs (host-only;
- * touches no device). Same validation of shapes/count/dtype as above.
+ * touches no device): lets a caller check the footprint before a call. Same
+ * validation of shapes/count/dtype as ns_orthogonalize_batched, including the
+ * too-large-for-the-tiled-path NS_EINVAL.
  */
 ns_status ns_workspace_bytes(const int64_t* shapes, int32_t count,
                              int32_t dtype, size_t* out_bytes);
 
 /*
- * Free the workspace and plan cache held for (current device, stream).
- * Device memory is released with stream-ordered frees on `stream`, so this is
- * safe while earlier calls are in flight; the pinned host staging buffers are
- * freed after a host wait for their pending uploads. Returns NS_OK if nothing
- * was held.
+ * Free the workspace and plan cache held for (current device, stream): the
+ * ownership half of the per-stream workspace that ns_orthogonalize_batched
+ * grows on demand. Device memory is released with stream-ordered frees on
+ * `stream`, so this is safe while earlier calls are in flight; the pinned
+ * host staging buffers are freed after a host wait for their pending uploads
+ * (the one entry point that waits). Returns NS_OK if nothing was held.
  */
 ns_status ns_release_workspace(void* stream);
 
-/* Message of the last non-OK status on the calling thread ("" if none). */
+/* Message of the last non-OK status on the calling thread ("" if none): the
+ * error channel of every entry point above. The string stays valid until the
+ * thread's next call into the library. */
 const char* ns_last_error(void);
 
 /* Library version string. */

@@ -17,22 +17,27 @@ hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
                         const CoeffTable& coeffs, int xl_floats, hipStream_t stream);
 
 // Sum of squares of each large matrix in kNormChunk pieces (one workgroup per
-// piece) ...
+// piece; partials holds 2 total_parts floats: the pieces' scaled sums, then
+// their power-of-two exponents) ...
 hipError_t launch_norm_partial(int dtype, const LargeMat* mats, int nmats,
                                const int32_t* part_prefix, int total_parts,
                                float* partials, hipStream_t stream);
-// ... then one workgroup per matrix folds its pieces into
-// inv[i] = 1 / (sqrt(sum) + 1e-7).
+// ... then one workgroup per matrix folds its pieces in a fixed order into
+// the pair inv[2i] = 1 / (sqrt(T) + 1e-7 2^E), inv[2i + 1] = 2^E, where
+// ||G||^2 = T 2^(-2E) (E = 0 unless G has entries of 2^40 or more), so that
+// X = (G 2^E) inv[2i].
 hipError_t launch_norm_final(int nmats, const int32_t* part_prefix,
-                             const float* partials, float* inv, hipStream_t stream);
+                             const float* partials, int total_parts, float* inv,
+                             hipStream_t stream);
 
-// X = G * inv, transposed when rows > cols, zero-padded to mp x np; writes the
-// fp32 master (bf16 path), X and X^T operand copies (slot 0).
+// X = G / (||G|| + eps), transposed when rows > cols, zero-padded to mp x np.
+// bf16: writes X^T as X_hi = bf16(X) (column panels, slot 0) and
+// X_lo = bf16(X - X_hi); fp32: writes X^T and X (slot 0).
 hipError_t launch_prep(int dtype, const LargeMat* mats, int nmats,
                        const int32_t* prep_prefix, int total_prep,
                        const float* inv, hipStream_t stream);
 
-// steps == 0: G <- G * inv in place.
+// steps == 0: G <- G / (||G|| + eps) in place.
 hipError_t launch_scale_out(int dtype, const LargeMat* mats, int nmats,
                             const int32_t* part_prefix, int total_parts,
                             const float* inv, hipStream_t stream);

@@ -242,3 +242,23 @@ def test_workspace_bytes():
     data = 2 * np_ * ldt + 2 * 2 * np_ * ldt + 2 * 2 * mp * ldt
     assert data <= b <= data + (1 << 20)
     assert ns.workspace_bytes([(0, 3)], ns.NS_BF16) <= 4096   # metadata only
+
+
+@pytest.mark.parametrize("shape,dtype,ok", [
+    ((8192, 65536), 0, True), ((10240, 10240), 0, True), ((65536, 8192), 0, True),
+    ((8192, 131072), 0, False), ((32768, 32768), 0, False), ((131072, 8192), 0, False),
+    ((8192, 65536), 1, False), ((4096, 65536), 1, True),
+    # a matrix of the small path (min dim <= 32) has no tiled-path limit
+    ((32, 1 << 24), 0, True),
+])
+def test_tiled_path_size_limit(shape, dtype, ok):
+    # the padded operand (np x mp elements) and a 256-row block of it must
+    # fit 32-bit buffer offsets: np mp elt < 2^31 and np 256 elt < 2^31
+    if ok:
+        assert ns.workspace_bytes([shape], dtype) > 0
+        assert ns.plan_classify([shape], dtype) == [1 if min(shape) <= 32 else 2]
+    else:
+        with pytest.raises(ns.NSError) as ei:
+            ns.workspace_bytes([shape], dtype)
+        assert ei.value.status == 1
+        assert "too large for the tiled path" in ns.last_error()
