@@ -15,7 +15,7 @@
 // Nothing here waits for the device. Workspace growth uses stream-ordered
 // allocation (hipMallocAsync / hipFreeAsync); metadata goes up from pinned
 // host slots that are reused only once their copy has completed (checked with
-// hipEventQuery, never waited on).
+// hipEventQuery, never waited on; a new slot is taken when none is free).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -120,8 +120,13 @@ struct Context {
     uint64_t clock = 0;
 };
 
-constexpr size_t kMaxCachedPlans = 16;
-constexpr size_t kMaxSlots = 8;
+// Batches whose plan and uploaded metadata a context keeps (least recently
+// used goes first).
+constexpr size_t kMaxCachedPlans = 64;
+// Pinned metadata staging per context: slots of at least kSlotMinBytes, at
+// most kMaxPinnedBytes in all.
+constexpr size_t kSlotMinBytes = size_t(1) << 20;
+constexpr size_t kMaxPinnedBytes = size_t(256) << 20;
 
 std::mutex g_ctx_mu;
 std::map<std::pair<int, uintptr_t>, std::unique_ptr<Context>> g_ctx;
@@ -175,25 +180,34 @@ ns_status ensure_workspace(Context* c, size_t bytes)
 }
 
 // A pinned host slot of at least `bytes` whose previous copy has finished.
+// Never waits: a slot still feeding a copy is skipped (hipEventQuery), and
+// when none is free a new one is allocated, up to kMaxPinnedBytes per
+// context; past that the call fails with NS_ENOMEM rather than block. (Slots
+// are only freed by ns_release_workspace: freeing pinned memory can wait for
+// the device.) A plan-cache hit uploads nothing, so an optimizer loop over a
+// fixed set of batches takes slots only on its first pass.
 PinnedSlot* get_slot(Context* c, size_t bytes, std::string* err)
 {
+    PinnedSlot* best = nullptr;
+    size_t held = 0;
     for (PinnedSlot& s : c->slots) {
-        if (s.cap < bytes)
+        held += s.cap;
+        if (s.cap < bytes || (best && best->cap <= s.cap))
             continue;
         if (!s.used || hipEventQuery(s.done) == hipSuccess)
-            return &s;
+            best = &s;   // the smallest free slot that fits
     }
-    if (c->slots.size() >= kMaxSlots) {
-        // Every slot is still in flight: wait for the oldest-sized fitting one.
-        for (PinnedSlot& s : c->slots) {
-            if (s.cap >= bytes) {
-                (void)hipEventSynchronize(s.done);
-                return &s;
-            }
-        }
-    }
+    if (best)
+        return best;
     PinnedSlot s;
-    s.cap = bytes < (1u << 20) ? (1u << 20) : bytes;
+    s.cap = bytes < kSlotMinBytes ? kSlotMinBytes : bytes;
+    if (held + s.cap > kMaxPinnedBytes) {
+        *err = "metadata staging: " + std::to_string(c->slots.size()) + " pinned buffers (" +
+               std::to_string(held >> 20) + " MiB) all feed pending uploads; a further " +
+               std::to_string(s.cap) + " bytes would pass the " + std::to_string(kMaxPinnedBytes >> 20) +
+               " MiB cap";
+        return nullptr;
+    }
     if (hipHostMalloc(&s.host, s.cap, hipHostMallocDefault) != hipSuccess) {
         (void)hipGetLastError();
         *err = "hipHostMalloc failed";
@@ -201,6 +215,7 @@ PinnedSlot* get_slot(Context* c, size_t bytes, std::string* err)
     }
     if (hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess) {
         (void)hipGetLastError();
+        (void)hipHostFree(s.host);
         *err = "hipEventCreate failed";
         return nullptr;
     }
@@ -467,7 +482,7 @@ ns_status run(Context* c, const int64_t* shapes, const Layout& L, int32_t count,
     });
     if (e == hipSuccess)
         e = timed(ns::kKindNormFinal, stream, [&] {
-            return ns::launch_norm_final(nl, part_prefix, partials, inv, stream);
+            return ns::launch_norm_final(nl, part_prefix, partials, p.total_parts, inv, stream);
         });
     if (e != hipSuccess)
         return hip_fail(e, "norm kernel launch");
