@@ -157,6 +157,45 @@ __device__ __forceinline__ int find_mat(const int32_t* prefix, int nmats, int b)
     return lo;
 }
 
+// Power-of-two scaling of the norm's squares. A piece of the sum of squares
+// whose largest magnitude is f 2^e (f in [0.5, 1)) with e > kNormScaleExp is
+// summed as (x 2^k)^2 with k = -min(e, 126), so its values lie below 4 and no
+// square or sum overflows fp32; k = 0 (no scaling) otherwise, and for Inf or
+// NaN, which then propagate. Scaling by 2^k is exact for normal values, so
+// where nothing overflows the bits are those of the unscaled sum.
+constexpr int kNormScaleExp = 40;
+__device__ __forceinline__ int norm_piece_exp(float mx)
+{
+    if (!(mx < __builtin_inff()))
+        return 0;
+    int e = 0;
+    (void)frexpf(mx, &e);
+    return e > kNormScaleExp ? -(e < 126 ? e : 126) : 0;
+}
+
+// Scale of a matrix from its pieces: E = min k_p, T = sum_p s_p 2^(2 (E - k_p))
+// (so ||G||^2 = T 2^(-2E)). Returns (1 / (sqrt(T) + eps 2^E), 2^E): X is
+// (G 2^E) times the first, i.e. G / (||G|| + eps) up to one rounding, and with
+// E = 0 exactly the unscaled 1 / (sqrt(sum) + eps).
+__device__ __forceinline__ float2 norm_scale(float t, int e)
+{
+    return make_float2(1.f / (sqrtf(t) + ldexpf(kEps, e)), ldexpf(1.f, e));
+}
+
+// Largest value over a 256-thread workgroup (order-free: max is exact).
+__device__ __forceinline__ float block_max(float v, float* red4)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red4[w] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+}
+
 // ---------------------------------------------------------------------------
 // Small matrices: m <= 32. One 256-thread workgroup runs the whole iteration.
 //   A = X X^T : 64 threads own a 4x4 block of the 32x32 A each; the four
@@ -206,11 +245,27 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
     NS_GLOBAL float* xw = gbl(S.xw);
     auto gat = [&](int64_t r) { return gbl(grow<T>(g, S.rows_tab, cols, r)); };
 
-    // ||G||_F over G's own row-major order: thread t takes elements t, t+512, ...
+    // ||G||_F over G's own row-major order: thread t takes elements t, t+512,
+    // ..., scaled by a power of two when the largest entry is huge (see
+    // norm_piece_exp; the whole matrix is one piece)
     const int64_t numel = S.rows * S.cols;
+    float mx = 0.f;
+    for (int64_t e = tid; e < numel; e += kSmallThreads)
+        mx = fmaxf(mx, fabsf(to_f32(gat(e / cols)[e % cols])));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if ((tid & 63) == 0)
+        red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])),
+               fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
+    __syncthreads();
+    const int k2 = norm_piece_exp(mx);
+    const float p2 = ldexpf(1.f, k2);
     float s = 0.f;
     for (int64_t e = tid; e < numel; e += kSmallThreads) {
-        const float v = to_f32(gat(e / cols)[e % cols]);
+        const float v = to_f32(gat(e / cols)[e % cols]) * p2;
         s = fmaf(v, v, s);
     }
     s = wave_sum(s);
@@ -218,13 +273,13 @@ __device__ __forceinline__ void small_body(const SmallMat& S, int steps, const C
         red[tid >> 6] = s;
     __syncthreads();
     s = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
-    const float inv = 1.f / (sqrtf(s) + kEps);
-    // X = G inv, oriented m x n (rows MR - m .. stay zero)
+    const float inv = norm_scale(s, k2).x;
+    // X = (G 2^k) inv, oriented m x n (rows MR - m .. stay zero)
     for (int e = tid; e < MR * n; e += kSmallThreads) {
         const int i = e / n, j = e - (e / n) * n;
         float v = 0.f;
         if (i < m)
-            v = to_f32(S.trans ? gat(j)[i] : gat(i)[j]) * inv;
+            v = to_f32(S.trans ? gat(j)[i] : gat(i)[j]) * p2 * inv;
         if (XL)
             xs[j * LX + i] = v;
         else if (i < m)
@@ -395,11 +450,14 @@ __global__ __launch_bounds__(kSmallThreads) void k_small(const SmallMat* __restr
     }
 }
 
+// Norm, pass 1: one workgroup per kNormChunk-element piece of a matrix (in its
+// row-major order). partials[b] is the piece's sum of squares, scaled by
+// 2^(2 k) with k = partials[total + b] (see norm_piece_exp).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_norm_partial(const LargeMat* __restrict__ mats,
                                                            int nmats,
                                                            const int32_t* __restrict__ prefix,
-                                                           float* __restrict__ partials)
+                                                           float* __restrict__ partials, int total)
 {
     using T = typename Elt<DT>::type;
     __shared__ float red[4];
@@ -412,65 +470,88 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const LargeMat* __res
     const int64_t left = M.rows * M.cols - base;
     const T* g = static_cast<const T*>(M.user) + base;
     const int tid = threadIdx.x;
-    float s = 0.f;
+    // this thread's Q x V elements, in order (zeros past the matrix's end)
+    float f[Q][V];
     if (M.rows_tab) {
         // row blocks: the same elements in the same order, found row by row
-        for (int q = 0; q < Q; ++q) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const int64_t idx = (int64_t)(tid + kThreads * q) * V + e;
+                f[q][e] = 0.f;
                 if (idx < left) {
                     const int64_t flat = base + idx;
-                    const float f = to_f32(grow<const T>(nullptr, M.rows_tab, M.cols, flat / M.cols)[flat % M.cols]);
-                    s = fmaf(f, f, s);
+                    f[q][e] = to_f32(grow<const T>(nullptr, M.rows_tab, M.cols, flat / M.cols)[flat % M.cols]);
                 }
             }
-        }
     } else if (left >= kNormChunk && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
         typedef T vec_t __attribute__((ext_vector_type(V)));
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const vec_t v = *reinterpret_cast<const vec_t*>(g + (int64_t)(tid + kThreads * q) * V);
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const float f = to_f32(v[e]);
-                s = fmaf(f, f, s);
-            }
+            for (int e = 0; e < V; ++e)
+                f[q][e] = to_f32(v[e]);
         }
     } else {
-        for (int q = 0; q < Q; ++q) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const int64_t idx = (int64_t)(tid + kThreads * q) * V + e;
-                if (idx < left) {
-                    const float f = to_f32(g[idx]);
-                    s = fmaf(f, f, s);
-                }
+                f[q][e] = idx < left ? to_f32(g[idx]) : 0.f;
             }
-        }
     }
+    float mx = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            mx = fmaxf(mx, fabsf(f[q][e]));
+    const int k = norm_piece_exp(block_max(mx, red));
+    const float p2 = ldexpf(1.f, k);
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float v = f[q][e] * p2;
+            s = fmaf(v, v, s);
+        }
     s = block_sum(s, red);
-    if (tid == 0)
+    if (tid == 0) {
         partials[b] = s;
+        partials[total + b] = (float)k;
+    }
 }
 
-// Norm, pass 2: one workgroup per matrix; thread t adds pieces t, t+256, ...
+// Norm, pass 2: one workgroup per matrix. E = min over its pieces of k; the
+// pieces' sums brought to scale 2^(2E) are added in a fixed order (thread t
+// takes pieces t, t+256, ...). scale[2 mi], scale[2 mi + 1] = norm_scale.
 __global__ __launch_bounds__(kThreads) void k_norm_final(const int32_t* __restrict__ prefix,
-                                                         const float* __restrict__ partials,
-                                                         float* __restrict__ inv)
+                                                         const float* __restrict__ partials, int total,
+                                                         float* __restrict__ scale)
 {
     __shared__ float red[4];
     const int mi = blockIdx.x;
     const int p0 = prefix[mi], np = prefix[mi + 1] - p0;
+    float kmin = 0.f;
+    for (int i = threadIdx.x; i < np; i += kThreads)
+        kmin = fminf(kmin, partials[total + p0 + i]);
+    const int e = -(int)block_max(-kmin, red);
     float s = 0.f;
     for (int i = threadIdx.x; i < np; i += kThreads)
-        s += partials[p0 + i];
+        s += ldexpf(partials[p0 + i], 2 * (e - (int)partials[total + p0 + i]));
     s = block_sum(s, red);
-    if (threadIdx.x == 0)
-        inv[mi] = 1.f / (sqrtf(s) + kEps);
+    if (threadIdx.x == 0) {
+        const float2 sc = norm_scale(s, e);
+        scale[2 * mi] = sc.x;
+        scale[2 * mi + 1] = sc.y;
+    }
 }
 
-// steps == 0: G <- G * inv, same pieces as the norm.
+// steps == 0: G <- (G 2^E) inv, same pieces as the norm.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_scale_out(const LargeMat* __restrict__ mats,
                                                         int nmats,
@@ -483,12 +564,12 @@ __global__ __launch_bounds__(kThreads) void k_scale_out(const LargeMat* __restri
     const LargeMat& M = mats[mi];
     const int64_t base = (int64_t)(b - prefix[mi]) * kNormChunk;
     const int64_t left = M.rows * M.cols - base;
-    const float s = inv[mi];
+    const float s = inv[2 * mi], p2 = inv[2 * mi + 1];
     for (int i = threadIdx.x; i < kNormChunk; i += kThreads)
         if (i < left) {
             const int64_t flat = base + i;
             T* row = grow<T>(M.user, M.rows_tab, M.cols, flat / M.cols);
-            row[flat % M.cols] = from_f32<T>(to_f32(row[flat % M.cols]) * s);
+            row[flat % M.cols] = from_f32<T>(to_f32(row[flat % M.cols]) * p2 * s);
         }
 }
 
@@ -523,7 +604,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
     const int per_row = M.np / kPrepTile;
     const int64_t i0 = (int64_t)(local / per_row) * kPrepTile;
     const int64_t j0 = (int64_t)(local % per_row) * kPrepTile;
-    const float s = inv[mi];
+    // X = (G 2^E) s (see k_norm_final); 2^E = 1 unless G has huge entries
+    const float s = inv[2 * mi], p2 = inv[2 * mi + 1];
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     if constexpr (DT == 0) {
         if (M.trans) {
@@ -539,13 +621,13 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
                 const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + 8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    v[e] = (float)a[e] * s;
-                    v[8 + e] = (float)b[e] * s;
+                    v[e] = (float)a[e] * p2 * s;
+                    v[8 + e] = (float)b[e] * p2 * s;
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    v[e] = (j < M.n && i + e < M.m) ? to_f32(src[e]) * s : 0.f;
+                    v[e] = (j < M.n && i + e < M.m) ? to_f32(src[e]) * p2 * s : 0.f;
             }
             bf16x8 h[2], l[2];
 #pragma unroll
@@ -577,13 +659,13 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
                 const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + 8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    tile[r][16 * q + e] = (float)a[e] * s;
-                    tile[r][16 * q + 8 + e] = (float)b[e] * s;
+                    tile[r][16 * q + e] = (float)a[e] * p2 * s;
+                    tile[r][16 * q + 8 + e] = (float)b[e] * p2 * s;
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    tile[r][16 * q + e] = (i < M.m && j + e < M.n) ? to_f32(src[e]) * s : 0.f;
+                    tile[r][16 * q + e] = (i < M.m && j + e < M.n) ? to_f32(src[e]) * p2 * s : 0.f;
             }
             __syncthreads();
             bf16x8 h[2], l[2];
@@ -609,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
         for (int p = 0; p < 16; ++p) {
             const int r = ty + 4 * p;
             const int64_t i = i0 + r, j = j0 + tx;
-            const float v = (i < M.m && j < M.n) ? to_f32(grow<const T>(M.user, M.rows_tab, M.cols, i)[j]) * s : 0.f;
+            const float v = (i < M.m && j < M.n) ? to_f32(grow<const T>(M.user, M.rows_tab, M.cols, i)[j]) * p2 * s : 0.f;
             tile[r][tx] = v;
             put_x<T>(M, i, j, v);
         }
@@ -624,7 +706,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const LargeMat* __restrict__ 
         for (int p = 0; p < 16; ++p) {
             const int r = ty + 4 * p;
             const int64_t j = j0 + r, i = i0 + tx;
-            const float v = (i < M.m && j < M.n) ? to_f32(grow<const T>(M.user, M.rows_tab, M.cols, j)[i]) * s : 0.f;
+            const float v = (i < M.m && j < M.n) ? to_f32(grow<const T>(M.user, M.rows_tab, M.cols, j)[i]) * p2 * s : 0.f;
             tile[r][tx] = v;
             put_xt<T>(M, i, j, v);
         }
@@ -1770,17 +1852,18 @@ hipError_t launch_norm_partial(int dtype, const LargeMat* mats, int nmats, const
 {
     if (dtype == 0)
         hipLaunchKernelGGL(k_norm_partial<0>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
-                           nmats, part_prefix, partials);
+                           nmats, part_prefix, partials, total_parts);
     else
         hipLaunchKernelGGL(k_norm_partial<1>, dim3(total_parts), dim3(kThreads), 0, stream, mats,
-                           nmats, part_prefix, partials);
+                           nmats, part_prefix, partials, total_parts);
     return hipGetLastError();
 }
 
-hipError_t launch_norm_final(int nmats, const int32_t* part_prefix, const float* partials, float* inv,
-                             hipStream_t stream)
+hipError_t launch_norm_final(int nmats, const int32_t* part_prefix, const float* partials, int total_parts,
+                             float* inv, hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_norm_final, dim3(nmats), dim3(kThreads), 0, stream, part_prefix, partials, inv);
+    hipLaunchKernelGGL(k_norm_final, dim3(nmats), dim3(kThreads), 0, stream, part_prefix, partials, total_parts,
+                       inv);
     return hipGetLastError();
 }
 

@@ -325,10 +325,10 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
     off = align_up(off + sizeof(int32_t) * p.part_prefix.size());
     p.meta_prep_prefix = off;
     off = align_up(off + sizeof(int32_t) * p.prep_prefix.size());
-    p.meta_inv = off;
-    off = align_up(off + sizeof(float) * p.large.size());
-    p.meta_partials = off;
-    off = align_up(off + sizeof(float) * (size_t)p.total_parts);
+    p.meta_inv = off;   // (scale, 2^E) per matrix
+    off = align_up(off + 2 * sizeof(float) * p.large.size());
+    p.meta_partials = off;   // scaled sums, then exponents, per piece
+    off = align_up(off + 2 * sizeof(float) * (size_t)p.total_parts);
     p.meta_end = off;
     return 0;
 }
