@@ -2,7 +2,9 @@
 
 The fp64 oracle needs minutes per 8192x6144 matrix, so it ran once on a seeded
 sample of each workload's matrices (tests/golden/make_oracle_golden.py) and
-stored sampled output rows plus a +-1 sketch of the whole result. Here the
+stored one output row per 256-row band, one output column per 256-column band
+(a row and a column through every output tile) and a +-1 sketch of the whole
+result. Here the
 whole batch runs in one call, at the shapes the benchmark times; the sampled
 matrices are compared with the stored oracle values, and properties that hold
 at any size are checked on every matrix (finite values, exact zero padding,
@@ -47,7 +49,7 @@ def _check_sample(name, mat_cpu, y_dev):
     assert g is not None
     assert str(g["input_sha256"]) == workloads.sha256(mat_cpu), "input differs from the oracle's"
     e = check_against_golden(y_dev.cpu(), g)
-    print(f"{name}: rows {e[0]:.3e} sketch {e[1]:.3e} norm {e[2]:.3e}", flush=True)
+    print(f"{name}: rows {e[0]:.3e} sketch {e[1]:.3e} norm {e[2]:.3e} worst row/col {e[3]:.3e}", flush=True)
 
 
 def test_dense_lowrank_batch():
