@@ -188,6 +188,38 @@ ns_status ns_orthogonalize_chunked(void* const* chunk_ptrs, const int64_t* chunk
                                    const float* coeffs, int32_t dtype,
                                    void* stream);
 
+/* Device scratch of ns_orthogonalize_batched_noalloc, per device. */
+#define NS_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/*
+ * As ns_orthogonalize_batched (same arguments, results bit for bit the same),
+ * for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. This call makes no device
+ * or pinned-host allocation (no hipMalloc, hipMallocAsync, hipHostMalloc or
+ * hipFree of any kind) and never waits for the device.
+ *
+ * Workspace: a static device array of NS_NOALLOC_SCRATCH_BYTES that each
+ * device this library runs on holds until the process ends (reserved when
+ * the library's code is loaded on the device). The batch's workspace and
+ * metadata must fit it: ns_workspace_bytes(shapes, count, dtype) + 256 <=
+ * NS_NOALLOC_SCRATCH_BYTES (e.g. the 32 attention-gate matrices of 24 x 2304,
+ * or one 2048 x 6144 bf16 matrix); a larger batch is rejected with NS_EINVAL
+ * before anything is enqueued. The metadata goes up through kernel
+ * arguments (one small copy kernel per 2 KB).
+ *
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device race (two streams, or two
+ * host threads); calls on one stream are ordered by it. Nothing in the array
+ * needs to start at any value.
+ *
+ * Errors as ns_orthogonalize_batched, plus NS_EINVAL for a batch that does
+ * not fit the scratch array.
+ */
+ns_status ns_orthogonalize_batched_noalloc(void* const* ptrs, const int64_t* shapes,
+                                           int32_t count, int32_t steps,
+                                           const float* coeffs, int32_t dtype,
+                                           void* stream);
+
 /*
  * Placement of whole matrices onto `world` data-parallel ranks (host-only; no
  * device is touched): which rank orthogonalizes each matrix and where it sits

@@ -13,6 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libns.so")
 
 NS_BF16, NS_FP32 = 0, 1
+# device scratch of ns_orthogonalize_batched_noalloc (NS_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 STATUS = {0: "NS_OK", 1: "NS_EINVAL", 2: "NS_EDTYPE", 3: "NS_ENOMEM", 4: "NS_EHIP"}
 QUINTIC = (3.4445, -4.7750, 2.0315)
 PROFILE_KINDS = ("norm_partial", "norm_final", "prep", "syrk", "poly", "update",
@@ -42,6 +44,8 @@ def lib() -> ctypes.CDLL:
     L.ns_orthogonalize_batched.restype = ctypes.c_int
     L.ns_orthogonalize_batched_sched.argtypes = L.ns_orthogonalize_batched.argtypes
     L.ns_orthogonalize_batched_sched.restype = ctypes.c_int
+    L.ns_orthogonalize_batched_noalloc.argtypes = L.ns_orthogonalize_batched.argtypes
+    L.ns_orthogonalize_batched_noalloc.restype = ctypes.c_int
     L.ns_orthogonalize_chunked.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32),
                                            ctypes.POINTER(i64), i32, i32, ctypes.POINTER(ctypes.c_float),
                                            i32, vp]
@@ -104,12 +108,12 @@ def _is_schedule(coeffs) -> bool:
 
 
 def orthogonalize_raw(ptrs, shapes, steps: int, coeffs, dtype: int, stream: int = 0,
-                      count: Optional[int] = None) -> int:
-    """Direct call of ns_orthogonalize_batched (one (a, b, c) triple) or of
-    ns_orthogonalize_batched_sched (a sequence of triples, one per step);
-    returns the status code. `ptrs` are integers (device addresses; 0 = NULL),
-    `shapes` (rows, cols) pairs; None for either passes NULL. For contract
-    tests."""
+                      count: Optional[int] = None, noalloc: bool = False) -> int:
+    """Direct call of ns_orthogonalize_batched (one (a, b, c) triple), of
+    ns_orthogonalize_batched_sched (a sequence of triples, one per step) or,
+    with noalloc, of ns_orthogonalize_batched_noalloc; returns the status
+    code. `ptrs` are integers (device addresses; 0 = NULL), `shapes` (rows,
+    cols) pairs; None for either passes NULL. For contract tests."""
     n = len(shapes) if count is None else count
     p = None if ptrs is None else (ctypes.c_void_p * max(1, len(ptrs)))(*[v or None for v in ptrs])
     s = None if shapes is None else _shapes_array(shapes)
@@ -119,14 +123,17 @@ def orthogonalize_raw(ptrs, shapes, steps: int, coeffs, dtype: int, stream: int 
         c = (ctypes.c_float * max(1, len(flat)))(*flat)
         return int(lib().ns_orthogonalize_batched_sched(p, s, n, steps, c, dtype, st))
     c = None if coeffs is None else (ctypes.c_float * 3)(*coeffs)
+    if noalloc:
+        return int(lib().ns_orthogonalize_batched_noalloc(p, s, n, steps, c, dtype, st))
     return int(lib().ns_orthogonalize_batched(p, s, n, steps, c, dtype, st))
 
 
-def orthogonalize(tensors, steps: int = 5, coeffs=QUINTIC, stream=None):
+def orthogonalize(tensors, steps: int = 5, coeffs=QUINTIC, stream=None, noalloc: bool = False):
     """Orthogonalize a list of 2-D CUDA tensors (all bf16 or all fp32) in place
     on `stream` (default: the current stream). `coeffs` is one (a, b, c)
     triple for every step, or a sequence of `steps` triples (a schedule).
-    Returns the list."""
+    noalloc: use ns_orthogonalize_batched_noalloc (one triple only; the batch
+    must fit NS_NOALLOC_SCRATCH_BYTES). Returns the list."""
     import torch
     tensors = list(tensors)
     if not tensors:
@@ -154,7 +161,9 @@ def orthogonalize(tensors, steps: int = 5, coeffs=QUINTIC, stream=None):
         s = torch.cuda.current_stream() if stream is None else stream
         if _is_schedule(coeffs) and len(coeffs) != steps:
             raise ValueError("a coefficient schedule needs one (a, b, c) triple per step")
-        rc = orthogonalize_raw(ptrs, shapes, steps, coeffs, code, s.cuda_stream)
+        if noalloc and _is_schedule(coeffs):
+            raise ValueError("the no-allocation entry point takes one (a, b, c) triple")
+        rc = orthogonalize_raw(ptrs, shapes, steps, coeffs, code, s.cuda_stream, noalloc=noalloc)
     _check(rc)
     return tensors
 

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libns.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["ns_kernels.hip", "ns_api.cpp", "ns_plan.cpp", "ns_ranks.cpp"]
+SOURCES = ["ns_kernels.hip", "ns_api.cpp", "ns_noalloc.hip", "ns_plan.cpp", "ns_ranks.cpp"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

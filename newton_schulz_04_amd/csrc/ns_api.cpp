@@ -30,14 +30,15 @@
 #include <vector>
 
 #include "ns.h"
+#include "ns_enqueue.h"
 #include "ns_kernels.h"
 #include "ns_plan.h"
 
 namespace {
-
-using ns::Plan;
-
 thread_local std::string g_last_error;
+}  // namespace
+
+namespace ns {
 
 ns_status fail(ns_status s, const std::string& msg)
 {
@@ -49,6 +50,17 @@ ns_status hip_fail(hipError_t e, const char* what)
 {
     return fail(NS_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace ns
+
+namespace {
+
+using ns::Plan;
+using ns::fail;
+using ns::hip_fail;
+using ns::Layout;
 
 // --- profiling --------------------------------------------------------------
 struct ProfRec {
@@ -83,18 +95,6 @@ struct PinnedSlot {
     size_t cap = 0;
     hipEvent_t done = nullptr;
     bool used = false;
-};
-
-// Where the caller's matrices live: one contiguous row-major buffer each, or
-// (chunked) a vertical stack of row blocks, matrix i taking the next
-// nchunks[i] blocks of chunk_ptrs / chunk_rows.
-struct Layout {
-    void* const* ptrs = nullptr;
-    void* const* chunk_ptrs = nullptr;
-    const int64_t* chunk_rows = nullptr;
-    const int32_t* nchunks = nullptr;
-    int32_t total_chunks = 0;
-    bool chunked() const { return chunk_ptrs != nullptr; }
 };
 
 struct CachedPlan {
@@ -223,6 +223,10 @@ PinnedSlot* get_slot(Context* c, size_t bytes, std::string* err)
     return &c->slots.back();
 }
 
+}  // namespace
+
+namespace ns {
+
 // Host image of the metadata block [0, meta_inv).
 // Row tables of a chunked call, placed after the plan's metadata: matrix i's
 // table (rows pointers) at rowtab_off[i] of the block; returns the bytes.
@@ -331,6 +335,10 @@ void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* m
     std::memcpy(h + p.meta_part_prefix, p.part_prefix.data(), p.part_prefix.size() * sizeof(int32_t));
     std::memcpy(h + p.meta_prep_prefix, p.prep_prefix.data(), p.prep_prefix.size() * sizeof(int32_t));
 }
+
+}  // namespace ns
+
+namespace {
 
 bool same_key(const CachedPlan& cp, const int64_t* shapes, const Layout& L, int32_t count,
               int32_t dtype, void* ws)
@@ -442,8 +450,16 @@ ns_status run(Context* c, const int64_t* shapes, const Layout& L, int32_t count,
         hit = &c->plans.back();
     }
     hit->last_use = ++c->clock;
-    const Plan& p = *hit->plan;
-    char* meta = static_cast<char*>(hit->meta);
+    return ns::enqueue(*hit->plan, static_cast<char*>(hit->meta), steps, coeffs, per_step, dtype, stream);
+}
+
+}  // namespace
+
+namespace ns {
+
+ns_status enqueue(const Plan& p, char* meta, int32_t steps, const float* coeffs, int32_t per_step,
+                  int32_t dtype, hipStream_t stream)
+{
     auto* large = reinterpret_cast<const ns::LargeMat*>(meta + p.meta_large);
     auto* small = reinterpret_cast<const ns::SmallMat*>(meta + p.meta_small);
     auto* syrk = reinterpret_cast<const ns::Tile*>(meta + p.meta_syrk);
@@ -528,7 +544,7 @@ ns_status run(Context* c, const int64_t* shapes, const Layout& L, int32_t count,
     return NS_OK;
 }
 
-}  // namespace
+}  // namespace ns
 
 extern "C" {
 
@@ -577,11 +593,11 @@ static ns_status check_dims(int32_t i, int64_t r, int64_t c)
     return NS_OK;
 }
 
-static ns_status orthogonalize(void* const* ptrs, const int64_t* shapes, int32_t count,
-                               int32_t steps, const float* coeffs, int32_t per_step,
-                               int32_t dtype, void* stream)
+}  // extern "C"
+
+ns_status ns::validate_batched(void* const* ptrs, const int64_t* shapes, int32_t count, int32_t steps,
+                               const float* coeffs, int32_t per_step, int32_t dtype)
 {
-    g_last_error.clear();
     ns_status st = check_common(count, steps, coeffs, per_step, dtype);
     if (st != NS_OK)
         return st;
@@ -599,6 +615,19 @@ static ns_status orthogonalize(void* const* ptrs, const int64_t* shapes, int32_t
         if (reinterpret_cast<uintptr_t>(ptrs[i]) % elt)
             return fail(NS_EINVAL, "matrix " + std::to_string(i) + " is not aligned to its element size");
     }
+    return NS_OK;
+}
+
+extern "C" {
+
+static ns_status orthogonalize(void* const* ptrs, const int64_t* shapes, int32_t count,
+                               int32_t steps, const float* coeffs, int32_t per_step,
+                               int32_t dtype, void* stream)
+{
+    g_last_error.clear();
+    ns_status st = ns::validate_batched(ptrs, shapes, count, steps, coeffs, per_step, dtype);
+    if (st != NS_OK)
+        return st;
     Layout L;
     L.ptrs = ptrs;
     return submit(shapes, L, count, steps, coeffs, per_step, dtype, stream);

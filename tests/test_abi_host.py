@@ -262,3 +262,18 @@ def test_tiled_path_size_limit(shape, dtype, ok):
             ns.workspace_bytes([shape], dtype)
         assert ei.value.status == 1
         assert "too large for the tiled path" in ns.last_error()
+
+
+def test_noalloc_validation_without_device():
+    # argument errors and a batch too large for the static scratch array are
+    # reported before any device is touched
+    fake = 1 << 40
+    q = ns.QUINTIC
+    assert ns.orthogonalize_raw([fake], [(8192, 6144)], 5, q, ns.NS_BF16, noalloc=True) == 1
+    assert "no-allocation" in ns.last_error()
+    assert ns.orthogonalize_raw([fake], [(-1, 4)], 5, q, ns.NS_BF16, noalloc=True) == 1
+    assert ns.orthogonalize_raw([fake], [(300, 520)], 5, None, ns.NS_BF16, noalloc=True) == 1
+    assert ns.orthogonalize_raw([fake], [(300, 520)], 5, q, 9, noalloc=True) == 2
+    assert ns.orthogonalize_raw([fake + 1], [(300, 520)], 5, q, ns.NS_BF16, noalloc=True) == 1
+    assert ns.orthogonalize_raw([0], [(0, 520)], 5, q, ns.NS_BF16, noalloc=True) == 0
+    assert ns.orthogonalize_raw([fake], [(1 << 25, 4)], 5, q, ns.NS_BF16, noalloc=True) == 1
