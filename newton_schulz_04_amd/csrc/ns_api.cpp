@@ -314,6 +314,7 @@ void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* m
     }
     for (size_t si = 0; si < p.small.size(); ++si) {
         const ns::PlanMat& pm = p.mats[p.small[si]];
+        const ns::SmallOffsets& so = p.small_off[si];
         ns::SmallMat d{};
         d.user = user[pm.index];
         d.rows_tab = tab[pm.index];
@@ -323,7 +324,12 @@ void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* m
         d.n = pm.n;
         d.trans = pm.trans;
         d.batch_index = pm.index;
-        d.xw = reinterpret_cast<float*>(ws + p.small_off[si]);
+        d.mr = so.mr;
+        d.nslices = so.nslices;
+        d.slice_cols = so.slice_cols;
+        d.slice_begin = p.small_prefix[si];
+        d.gram = reinterpret_cast<double*>(ws + so.gram);
+        d.norm = reinterpret_cast<double*>(ws + so.norm);
         std::memcpy(h + p.meta_small + si * sizeof(ns::SmallMat), &d, sizeof d);
     }
     if (!p.syrk_run.empty())
@@ -334,6 +340,7 @@ void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* m
         std::memcpy(h + p.meta_update, p.update_tiles.data(), p.update_tiles.size() * sizeof(ns::Tile));
     std::memcpy(h + p.meta_part_prefix, p.part_prefix.data(), p.part_prefix.size() * sizeof(int32_t));
     std::memcpy(h + p.meta_prep_prefix, p.prep_prefix.data(), p.prep_prefix.size() * sizeof(int32_t));
+    std::memcpy(h + p.meta_small_prefix, p.small_prefix.data(), p.small_prefix.size() * sizeof(int32_t));
 }
 
 }  // namespace ns
@@ -475,21 +482,37 @@ ns_status enqueue(const Plan& p, char* meta, int32_t steps, const float* coeffs,
 
     hipError_t e = hipSuccess;
     if (!p.small.empty()) {
-        ns::CoeffTable table{};
-        table.per_step = per_step;
-        for (int s = 0; s < (per_step ? steps : (steps > 0 ? 1 : 0)); ++s)
+        // norm pieces, Gram pieces, then the m x m recurrence and the
+        // result; a batch of one-slice matrices needs the first only
+        auto* small_prefix = reinterpret_cast<const int32_t*>(meta + p.meta_small_prefix);
+        const int ns_ = (int)p.small.size();
+        ns::SmallCoeffs co{};
+        co.per_step = per_step;
+        for (int s = 0; s < (per_step ? steps : std::min(steps, 1)); ++s)   // steps <= 64 when per_step
             for (int k = 0; k < 3; ++k)
-                table.v[s][k] = coef(s, k);
-        int xl = 0;
-        for (int32_t idx : p.small) {
-            const ns::PlanMat& pm = p.mats[idx];
-            xl = std::max(xl, ns::small_xl_floats(pm.m, pm.n));
+                co.v[3 * s + k] = coef(s, k);
+        // one launch per MR group (the planner orders small matrices by MR)
+        // and phase; a group of one-slice matrices needs only phase 0
+        hipError_t e2 = hipSuccess;
+        const int nphase = steps > 0 ? 3 : 2;
+        for (int phase = 0; phase < nphase && e2 == hipSuccess; ++phase) {
+            for (int i0 = 0; i0 < ns_ && e2 == hipSuccess;) {
+                int i1 = i0, most = 1;
+                while (i1 < ns_ && p.small_off[i1].mr == p.small_off[i0].mr)
+                    most = std::max(most, p.small_off[i1++].nslices);
+                if (phase == 0 || most > 1) {
+                    const int mr = p.small_off[i0].mr;
+                    const int nsl = p.small_prefix[i1] - p.small_prefix[i0];
+                    e2 = timed(ns::kKindSmall, stream, [&] {
+                        return ns::launch_small(dtype, mr, small + i0, i1 - i0, small_prefix + i0, nsl, phase,
+                                                steps, co, stream);
+                    });
+                }
+                i0 = i1;
+            }
         }
-        e = timed(ns::kKindSmall, stream, [&] {
-            return ns::launch_small(dtype, small, (int)p.small.size(), steps, table, xl, stream);
-        });
-        if (e != hipSuccess)
-            return hip_fail(e, "small-matrix kernel launch");
+        if (e2 != hipSuccess)
+            return hip_fail(e2, "small-matrix kernel launch");
     }
     if (nl == 0)
         return NS_OK;

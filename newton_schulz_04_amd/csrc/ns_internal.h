@@ -54,21 +54,34 @@ struct LargeMat {
     float* bdiag;      // bf16 path: B_ii - bf16(B_ii), mp floats
 };
 
-// Iteration coefficients for the fused small path, passed by value: step s
-// uses row s when per_step, else row 0 for every step.
+// Longest per-step coefficient schedule.
 constexpr int kMaxScheduleSteps = 64;
-struct CoeffTable {
-    float v[kMaxScheduleSteps][3];
+
+// (a, b, c) of the steps, passed by value to the small-path kernel: step s
+// uses v[3 s .. 3 s + 2] when per_step, else v[0 .. 2] (any step count).
+struct SmallCoeffs {
+    float v[3 * kMaxScheduleSteps];
     int32_t per_step;
 };
 
-// One matrix of the fused small path.
+// Small path (m <= kSmallMax): X's n columns are cut into slices of
+// slice_cols columns, kSmallSlice or, for very wide matrices, a multiple of it
+// that keeps a matrix at kSmallMaxSlices slices; one workgroup per slice and
+// phase (norm pieces; Gram pieces; the m x m recurrence and the result).
+constexpr int kSmallSlice = 512;
+constexpr int kSmallMaxSlices = 256;
+
+// One matrix of the small path.
 struct SmallMat {
     void* user;
     void* const* rows_tab;   // as in LargeMat
     int64_t rows, cols;
     int32_t m, n, trans, batch_index;
-    float* xw;         // fp32 working copy of X, m x n
+    int32_t mr;              // m rounded up to a multiple of 8
+    int32_t nslices, slice_cols;
+    int32_t slice_begin;     // its first workgroup in a small-path launch
+    double* gram;            // Gram pieces of X0 = G / (||G|| + eps): nslices x mr x mr
+    double* norm;            // norm pieces: nslices sums of squares
 };
 
 // Grouped-GEMM tile: matrix index into the LargeMat array and block coords.

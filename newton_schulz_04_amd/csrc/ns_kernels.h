@@ -8,13 +8,19 @@
 
 namespace ns {
 
-// Fused whole-iteration kernel for matrices with min dim <= kSmallMax, one
-// workgroup per matrix, fp32 arithmetic. X stays in LDS for matrices whose
-// small_xl_floats(m, n) is nonzero and at most `xl_floats` (the launch's LDS
-// share for it: the largest such value in the batch, or 0).
-int small_xl_floats(int m, int n);
-hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
-                        const CoeffTable& coeffs, int xl_floats, hipStream_t stream);
+// Small path (min dim <= kSmallMax, fp64 arithmetic): one workgroup per
+// column slice of each of `count` matrices (SmallMat, all with MR = mr,
+// whose slices are workgroups slice_prefix[0] .. slice_prefix[count]).
+//   phase 0   the slices' pieces of ||G||^2
+//   phase 1   X0 = G / (||G|| + eps) and the slices' pieces of A0 = X0 X0^T
+//             (with steps == 0: X0 written to the caller's buffer instead)
+//   phase 2   A0 from its pieces; the steps on the m x m matrices,
+//             B'_k = aI + b A_k + c A_k^2, Q <- B'_k Q, A_{k+1} = B'_k A_k B'_k;
+//             the caller's buffer <- Q X0
+// A matrix of one slice runs all of its phases in the phase-0 launch; when
+// every matrix has one slice, later phases need no launch.
+hipError_t launch_small(int dtype, int mr, const SmallMat* mats, int count, const int32_t* slice_prefix,
+                        int nslices, int phase, int steps, const SmallCoeffs& co, hipStream_t stream);
 
 // Sum of squares of each large matrix in kNormChunk pieces (one workgroup per
 // piece; partials holds 2 total_parts floats: the pieces' scaled sums, then

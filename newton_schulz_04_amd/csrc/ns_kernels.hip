@@ -5,9 +5,10 @@
 // then `steps` times A = X X^T, B = bA + cA^2, X = aX + BX.
 //
 // Kernels:
-//   k_small        whole iteration for min(rows, cols) <= 32, one workgroup of
-//                  512 threads per matrix, fp32 arithmetic, X resident in LDS
-//                  when it fits, else streamed from an L2-resident buffer.
+//   k_small        min(rows, cols) <= 32, fp64 arithmetic: the iteration
+//                  through the m x m Gram matrix (one Gram matrix, the steps
+//                  on m x m matrices, one product at the end); one 512-thread
+//                  workgroup per 512-column slice, three launches.
 //   k_norm_partial sum of squares of a 16K-element piece of G (wave shuffles).
 //   k_norm_final   folds the pieces of a matrix in fixed order -> 1/(||G||+eps).
 //   k_prep         X = G/(||G||+eps), transposed when rows > cols, zero-padded
@@ -30,9 +31,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
-#include <set>
-#include <utility>
 
 #include "ns_kernels.h"
 
@@ -197,257 +195,375 @@ __device__ __forceinline__ float block_max(float v, float* red4)
 }
 
 // ---------------------------------------------------------------------------
-// Small matrices: m <= 32. One 256-thread workgroup runs the whole iteration.
-//   A = X X^T : 64 threads own a 4x4 block of the 32x32 A each; the four
-//               wavefronts split every 64-column chunk of X by column
-//               (column j of a chunk goes to wavefront j % 4), and the four
-//               partial A's are added in wavefront order.
-//   B = bA + cA^2 in LDS.
-//   X <- aX + BX column by column; thread t owns columns t, t+256, ...
-// The fused small-matrix path (m <= 32). One workgroup per matrix runs the
-// whole iteration in fp32; X stays resident in LDS when it fits (column-major,
-// MR + 4 floats per column), else in an L2-resident workspace buffer that the
-// Gram pass streams through LDS in chunks of kSmallChunk columns, the next
-// chunk's loads in flight while the current one is multiplied. MR is m
-// rounded up to a multiple of 8: rows m .. MR - 1 are zero throughout, so
-// every product below is the exact m x m / m x n one plus zeros. Every sum
-// runs in a fixed order that depends only on (m, n).
-constexpr int kSmallThreads = 512;                // 8 wavefronts, 2 per SIMD
-constexpr int kSmallChunk = 128;
-constexpr int kSmallPartFloats = 8192;            // G x MR x MR Gram partials
-constexpr int kSmallSqFloats = 2 * 32 * 33;       // A and B, MR x (MR + 1)
-constexpr int kSmallXlMaxFloats = 28672;          // X resident in LDS up to 112 KB (156 KB in all)
-static_assert(4 * (kSmallPartFloats + kSmallSqFloats + 8 + kSmallXlMaxFloats) <= 160 * 1024,
-              "small-matrix kernel LDS exceeds the 160 KB of a compute unit");
+// Small matrices (m <= 32), fp64 arithmetic.
+//
+// Every step of the iteration multiplies X by an m x m polynomial in its own
+// Gram matrix: X_{k+1} = B'_k X_k with B'_k = aI + b A_k + c A_k^2 and
+// A_k = X_k X_k^T. Since X_k = Q_k X0 with Q_k = B'_{k-1} ... B'_0 (all of
+// them polynomials in A0, so symmetric and commuting), A_{k+1} =
+// B'_k A_k B'_k. The small path evaluates the iteration in that form: one
+// Gram matrix A0 = X0 X0^T over the n columns, the steps on m x m matrices,
+// and one product Q X0 at the end: 3 m^2 n + O(m^3) operations instead of
+// 4 m^2 n per step, and three launches whatever the step count. In exact
+// arithmetic it is the iteration itself; it runs in fp64 (whose vector rate
+// equals the unpacked fp32 one), so only the final rounding to the
+// caller's dtype is visible.
+//
+// X's n columns are cut into slices (SmallMat::slice_cols columns, 512 or a
+// multiple), one 512-thread workgroup per slice and launch, so a batch of
+// such matrices spreads over the device. Sums that cross slices (||G||^2,
+// A0) go through per-slice pieces in the workspace that the next phase
+// folds in slice order. MR is m rounded up to a multiple of 8: rows
+// m .. MR - 1 of X are zeros, so every product is the exact m x m / m x n one
+// plus zeros. Every sum has a fixed order that depends only on (m, n): a
+// matrix gives the same bits in any batch, and trailing zero rows leave the
+// others' bits unchanged.
+constexpr int kSmallThreads = 512;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallChunk = 256;          // columns of X0 per Gram chunk
+constexpr int kSmallPx = 34;              // doubles per X0 column in LDS (>= MR + 2, 16-byte rows)
+constexpr int kSmallPartDoubles = 8192;   // Gram pieces of the column groups
+constexpr double kEps64 = 1e-7;
+static_assert(kSmallSlice == kSmallThreads, "one column per thread in a full slice");
 
-template <int DT, int MR, bool XL>
-__device__ __forceinline__ void small_body(const SmallMat& S, int steps, const CoeffTable& coeffs, float* lds)
+struct SmallLds {
+    union {
+        struct {
+            double xs[kSmallChunk * kSmallPx];   // a chunk of X0's columns
+            double part[kSmallPartDoubles];      // Gram pieces per column group
+        } g;
+        double mats[6][32 * 32];                 // the m x m matrices, pitch MR
+    };
+    double red[kSmallWaves];
+};
+
+__device__ __forceinline__ double wave_sum_d(double v)
 {
-    using T = typename Elt<DT>::type;
-    constexpr int LD = MR + 1;                    // row pitch of A in LDS
-    constexpr int LX = MR + 4;                    // column pitch of X in LDS (16-byte aligned)
-    constexpr int NB = MR / 4;                    // 4 x 4 Gram blocks per edge
-    constexpr int NBLK = NB * NB;
-    constexpr int G = kSmallThreads / NBLK;       // column groups of the Gram pass
-    constexpr int QL = MR * kSmallChunk / kSmallThreads;   // chunk loads per thread
-    float* part = lds;                            // [G][MR][MR]
-    float* as = lds + kSmallPartFloats;           // [MR][LD]
-    // B at pitch MR: its reads in X <- aX + BX are the same for every lane,
-    // so 16-byte aligned rows let four of them go as one LDS read
-    float* bs = as + MR * LD;                     // [MR][MR]
-    float* red = lds + kSmallPartFloats + kSmallSqFloats;
-    float* xs = red + 8;                          // X (XL) or one chunk, [cols][LX]
-
-    const int tid = threadIdx.x;
-    const int m = S.m, n = S.n;
-    const int64_t cols = S.cols;
-    T* g = static_cast<T*>(S.user);
-    NS_GLOBAL float* xw = gbl(S.xw);
-    auto gat = [&](int64_t r) { return gbl(grow<T>(g, S.rows_tab, cols, r)); };
-
-    // ||G||_F over G's own row-major order: thread t takes elements t, t+512,
-    // ..., scaled by a power of two when the largest entry is huge (see
-    // norm_piece_exp; the whole matrix is one piece)
-    const int64_t numel = S.rows * S.cols;
-    float mx = 0.f;
-    for (int64_t e = tid; e < numel; e += kSmallThreads)
-        mx = fmaxf(mx, fabsf(to_f32(gat(e / cols)[e % cols])));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if ((tid & 63) == 0)
-        red[tid >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])),
-               fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
-    __syncthreads();
-    const int k2 = norm_piece_exp(mx);
-    const float p2 = ldexpf(1.f, k2);
-    float s = 0.f;
-    for (int64_t e = tid; e < numel; e += kSmallThreads) {
-        const float v = to_f32(gat(e / cols)[e % cols]) * p2;
-        s = fmaf(v, v, s);
-    }
-    s = wave_sum(s);
-    if ((tid & 63) == 0)
-        red[tid >> 6] = s;
-    __syncthreads();
-    s = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
-    const float inv = norm_scale(s, k2).x;
-    // X = (G 2^k) inv, oriented m x n (rows MR - m .. stay zero)
-    for (int e = tid; e < MR * n; e += kSmallThreads) {
-        const int i = e / n, j = e - (e / n) * n;
-        float v = 0.f;
-        if (i < m)
-            v = to_f32(S.trans ? gat(j)[i] : gat(i)[j]) * p2 * inv;
-        if (XL)
-            xs[j * LX + i] = v;
-        else if (i < m)
-            xw[e] = v;
-    }
-    __syncthreads();
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
 
-    const int blk = tid % NBLK, kg = tid / NBLK;
-    const int ti = blk / NB, tj = blk % NB;
-    const bool gram = kg < G;
-    // X <- aX + BX: RG threads share a column, each taking MR / RG rows
-    const int RG = XL ? (n <= 128 ? 4 : (n <= 256 ? 2 : 1)) : 1;
-    for (int step = 0; step < steps; ++step) {
-        const bool last = step == steps - 1;
-        const float* co = coeffs.v[coeffs.per_step ? step : 0];
-        const float ca = co[0], cb = co[1], cc = co[2];
-        float acc[4][4];
+// Sum over the workgroup in a fixed order; every thread gets it.
+__device__ __forceinline__ double block_sum_d(double v, double* red)
+{
+    v = wave_sum_d(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double t = red[0];
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+    for (int w = 1; w < kSmallWaves; ++w)
+        t += red[w];
+    return t;
+}
+
+// Element (r, c) of X = G or G^T, r < m, c < n, from the caller's buffer.
+template <typename T>
+__device__ __forceinline__ double small_g(const SmallMat& S, int r, int64_t c)
+{
+    return (double)to_f32(S.trans ? grow<const T>(S.user, S.rows_tab, S.cols, c)[r]
+                                  : grow<const T>(S.user, S.rows_tab, S.cols, r)[c]);
+}
+
+template <typename T>
+__device__ __forceinline__ void small_put(const SmallMat& S, int r, int64_t c, double v)
+{
+    if (S.trans)
+        gbl(grow<T>(S.user, S.rows_tab, S.cols, c))[r] = from_f32<T>((float)v);
+    else
+        gbl(grow<T>(S.user, S.rows_tab, S.cols, r))[c] = from_f32<T>((float)v);
+}
+
+// 1 / (||G|| + eps) from the slices' norm pieces (thread-strided, then the
+// workgroup, in a fixed order).
+__device__ __forceinline__ double small_inv(const SmallMat& S, double* red)
+{
+    const NS_GLOBAL double* nrm = gbl(S.norm);
+    double t = 0.0;
+    for (int i = threadIdx.x; i < S.nslices; i += kSmallThreads)
+        t += nrm[i];
+    t = block_sum_d(t, red);
+    return 1.0 / (sqrt(t) + kEps64);
+}
+
+// Phase 0: the slice's piece of ||G||^2. RG threads share a column (RG = 2
+// for n <= 256, else 1): thread t takes column t mod (512 / RG) of each
+// 512 / RG-column chunk and rows (t / (512 / RG)) MR / RG .. + MR / RG,
+// summed in order, then the workgroup in a fixed order.
+template <int DT, int MR, int RG>
+__device__ __forceinline__ void small_norm_piece(const SmallMat& S, int slice, SmallLds& L)
+{
+    using T = typename Elt<DT>::type;
+    constexpr int H = MR / RG, CW = kSmallThreads / RG;
+    const int tid = threadIdx.x, col = tid % CW, r0 = (tid / CW) * H;
+    const int m = S.m;
+    const int64_t c0 = (int64_t)slice * S.slice_cols;
+    const int64_t c1 = min(c0 + S.slice_cols, (int64_t)S.n);
+    double s = 0.0;
+    for (int64_t c = c0 + col; c < c1; c += CW) {
+        double v[H];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc[p][q] = 0.f;
-        auto gram_cols = [&](const float* xc, int ncols) __attribute__((always_inline)) {
-            if (!gram)
-                return;
+        for (int r = 0; r < H; ++r)
+            v[r] = r0 + r < m ? small_g<T>(S, r0 + r, c) : 0.0;
+#pragma unroll
+        for (int r = 0; r < H; ++r)
+            s = fma(v[r], v[r], s);
+    }
+    s = block_sum_d(s, L.red);
+    if (threadIdx.x == 0)
+        gbl(S.norm)[slice] = s;
+}
+
+// Phase 1: the slice's piece of A0 = X0 X0^T, in chunks of 256 columns of X0
+// staged in LDS (threads t and t + 256 fill the two halves of column t's
+// rows): 4 x 4 blocks of A0 per thread (NBLK = (MR / 4)^2 blocks), the
+// 512 / NBLK column groups summed in group order. With `out` (no steps) X0
+// goes to the caller's buffer instead.
+template <int DT, int MR>
+__device__ __forceinline__ void small_gram_piece(const SmallMat& S, int slice, bool out, SmallLds& L)
+{
+    using T = typename Elt<DT>::type;
+    constexpr int NB = MR / 4, NBLK = NB * NB, G = kSmallThreads / NBLK, MM = MR * MR, H = MR / 2;
+    static_assert(G * MM <= kSmallPartDoubles, "Gram pieces exceed their LDS");
+    const int tid = threadIdx.x, col = tid % kSmallChunk, r0 = (tid / kSmallChunk) * H;
+    const int m = S.m;
+    const int64_t c0 = (int64_t)slice * S.slice_cols;
+    const int64_t c1 = min(c0 + S.slice_cols, (int64_t)S.n);
+    const double inv = small_inv(S, L.red);
+    const int blk = tid % NBLK, kg = tid / NBLK, ti = blk / NB, tj = blk % NB;
+    double acc[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            acc[p][q] = 0.0;
+    for (int64_t cc0 = c0; cc0 < c1; cc0 += kSmallChunk) {
+        const int64_t c = cc0 + col;
+        const int ncols = (int)min((int64_t)kSmallChunk, c1 - cc0);
+        double x[H];
+#pragma unroll
+        for (int r = 0; r < H; ++r)
+            x[r] = (c < c1 && r0 + r < m) ? small_g<T>(S, r0 + r, c) * inv : 0.0;
+        if (out) {
+            if (c < c1) {
+#pragma unroll
+                for (int r = 0; r < H; ++r)
+                    if (r0 + r < m)
+                        small_put<T>(S, r0 + r, c, x[r]);
+            }
+            continue;
+        }
+#pragma unroll
+        for (int r = 0; r < H; r += 2)
+            *reinterpret_cast<double2*>(L.g.xs + col * kSmallPx + r0 + r) = make_double2(x[r], x[r + 1]);
+        __syncthreads();
+        if (kg < G) {
             for (int jj = kg; jj < ncols; jj += G) {
-                const f32x4 xr = *reinterpret_cast<const f32x4*>(xc + jj * LX + 4 * ti);
-                const f32x4 xq = *reinterpret_cast<const f32x4*>(xc + jj * LX + 4 * tj);
+                const double* xc = L.g.xs + jj * kSmallPx;
+                const double2 a0 = *reinterpret_cast<const double2*>(xc + 4 * ti);
+                const double2 a1 = *reinterpret_cast<const double2*>(xc + 4 * ti + 2);
+                const double2 b0 = *reinterpret_cast<const double2*>(xc + 4 * tj);
+                const double2 b1 = *reinterpret_cast<const double2*>(xc + 4 * tj + 2);
+                const double xr[4] = {a0.x, a0.y, a1.x, a1.y}, xq[4] = {b0.x, b0.y, b1.x, b1.y};
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        acc[p][q] = fmaf(xr[p], xq[q], acc[p][q]);
-            }
-        };
-        if (XL) {
-            gram_cols(xs, n);
-        } else {
-            // chunk c of X: element e = tid + 256 q is row e / CH, column e % CH
-            float pf[QL];
-            auto fetch = [&](int j0) __attribute__((always_inline)) {
-#pragma unroll
-                for (int q = 0; q < QL; ++q) {
-                    const int e = tid + kSmallThreads * q, r = e / kSmallChunk, jj = e % kSmallChunk;
-                    pf[q] = (r < m && j0 + jj < n) ? xw[(int64_t)r * n + j0 + jj] : 0.f;
-                }
-            };
-            fetch(0);
-            for (int j0 = 0; j0 < n; j0 += kSmallChunk) {
-#pragma unroll
-                for (int q = 0; q < QL; ++q) {
-                    const int e = tid + kSmallThreads * q;
-                    xs[(e % kSmallChunk) * LX + e / kSmallChunk] = pf[q];
-                }
-                __syncthreads();
-                if (j0 + kSmallChunk < n)
-                    fetch(j0 + kSmallChunk);
-                gram_cols(xs, kSmallChunk);
-                __syncthreads();
-            }
-        }
-        if (gram) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    part[(kg * MR + 4 * ti + p) * MR + 4 * tj + q] = acc[p][q];
-        }
-        __syncthreads();
-        for (int e = tid; e < MR * MR; e += kSmallThreads) {
-            float v = part[e];
-            for (int k = 1; k < G; ++k)
-                v += part[k * MR * MR + e];
-            as[(e / MR) * LD + e % MR] = v;
-        }
-        __syncthreads();
-        for (int e = tid; e < MR * MR; e += kSmallThreads) {
-            const int r = e / MR, c = e % MR;
-            float aa = 0.f;
-#pragma unroll
-            for (int t = 0; t < MR; ++t)
-                aa = fmaf(as[r * LD + t], as[t * LD + c], aa);
-            bs[r * MR + c] = cb * as[r * LD + c] + cc * aa;
-        }
-        __syncthreads();
-        // X <- aX + BX, column by column (the next column's loads in flight)
-        const int rg = tid % RG;
-        constexpr int MAXR = MR;
-        const int r0 = rg * (MR / RG), r1 = r0 + MR / RG;
-        const int jstep = kSmallThreads / RG;
-        float xn[MR];
-        auto load_col = [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-            for (int r = 0; r < MR; ++r)
-                xn[r] = j < n ? (XL ? xs[j * LX + r] : (r < m ? xw[(int64_t)r * n + j] : 0.f)) : 0.f;
-        };
-        int j = tid / RG;
-        load_col(j);
-        for (; j < n; j += jstep) {
-            float x[MAXR];
-#pragma unroll
-            for (int r = 0; r < MR; ++r)
-                x[r] = xn[r];
-            // (a column is read and rewritten only by its RG lanes, one
-            // wavefront, loads before stores; the next column is this
-            // thread's own)
-            load_col(j + jstep);
-#pragma unroll
-            for (int r = 0; r < MR; ++r) {
-                if (r >= r0 && r < r1 && r < m) {
-                    float y = ca * x[r];
-#pragma unroll
-                    for (int t = 0; t < MR; t += 4) {
-                        const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + r * MR + t);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            y = fmaf(b4[u], x[t + u], y);
-                    }
-                    if (!last) {
-                        if (XL)
-                            xs[j * LX + r] = y;
-                        else
-                            xw[(int64_t)r * n + j] = y;
-                    } else if (S.trans) {
-                        gat(j)[r] = from_f32<T>(y);
-                    } else {
-                        gat(r)[j] = from_f32<T>(y);
-                    }
-                }
+                        acc[p][q] = fma(xr[p], xq[q], acc[p][q]);
             }
         }
         __syncthreads();
     }
-    if (steps == 0) {
-        for (int e = tid; e < m * n; e += kSmallThreads) {
-            const int i = e / n, jj = e - (e / n) * n;
-            const float v = XL ? xs[jj * LX + i] : xw[e];
-            if (S.trans)
-                gat(jj)[i] = from_f32<T>(v);
-            else
-                gat(i)[jj] = from_f32<T>(v);
+    if (out)
+        return;
+    if (kg < G) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                L.g.part[(kg * MR + 4 * ti + p) * MR + 4 * tj + q] = acc[p][q];
+    }
+    __syncthreads();
+    NS_GLOBAL double* gq = gbl(S.gram) + (size_t)slice * MM;
+    for (int e = tid; e < MM; e += kSmallThreads) {
+        double v = L.g.part[e];
+        for (int k = 1; k < G; ++k)
+            v += L.g.part[k * MM + e];
+        gq[e] = v;
+    }
+}
+
+// Z = X^T Y for MR x MR matrices in LDS (pitch MR): with X symmetric, X Y.
+// Thread t < (MR / 2)^2 computes the 2 x 2 block (2 (t / (MR / 2)),
+// 2 (t mod (MR / 2))): each element sums X[k][i] Y[k][j] over k, even and odd
+// k apart, then their sum.
+template <int MR>
+__device__ __forceinline__ void small_mm(const double* X, const double* Y, double* Z)
+{
+    constexpr int NB = MR / 2;
+    const int t = threadIdx.x;
+    if (t < NB * NB) {
+        const int i0 = 2 * (t / NB), j0 = 2 * (t % NB);
+        double z[2][2][2] = {};
+#pragma unroll
+        for (int k = 0; k < MR; ++k) {
+            const double2 xa = *reinterpret_cast<const double2*>(X + k * MR + i0);
+            const double2 yb = *reinterpret_cast<const double2*>(Y + k * MR + j0);
+            z[k & 1][0][0] = fma(xa.x, yb.x, z[k & 1][0][0]);
+            z[k & 1][0][1] = fma(xa.x, yb.y, z[k & 1][0][1]);
+            z[k & 1][1][0] = fma(xa.y, yb.x, z[k & 1][1][0]);
+            z[k & 1][1][1] = fma(xa.y, yb.y, z[k & 1][1][1]);
+        }
+        *reinterpret_cast<double2*>(Z + i0 * MR + j0) = make_double2(z[0][0][0] + z[1][0][0], z[0][0][1] + z[1][0][1]);
+        *reinterpret_cast<double2*>(Z + (i0 + 1) * MR + j0) =
+            make_double2(z[0][1][0] + z[1][1][0], z[0][1][1] + z[1][1][1]);
+    }
+    __syncthreads();
+}
+
+// Phase 2: A0 from the slices' pieces (in slice order, eight pieces' loads
+// in flight at once); the steps on the m x m matrices; Y = Q X0 on the
+// slice's columns, written to the caller's buffer (RG threads per column as
+// in phase 0, each taking its rows).
+template <int DT, int MR, int RG>
+__device__ __forceinline__ void small_finish(const SmallMat& S, int slice, int steps, const SmallCoeffs& co,
+                                             SmallLds& L)
+{
+    using T = typename Elt<DT>::type;
+    constexpr int MM = MR * MR, H = MR / RG, CW = kSmallThreads / RG;
+    constexpr int EPT = (MM + kSmallThreads - 1) / kSmallThreads;
+    const int tid = threadIdx.x, col = tid % CW, r0 = (tid / CW) * H;
+    const int m = S.m;
+    const int64_t c0 = (int64_t)slice * S.slice_cols;
+    const int64_t c1 = min(c0 + S.slice_cols, (int64_t)S.n);
+    double* A = L.mats[0];
+    double* Sq = L.mats[1];
+    double* P = L.mats[2];
+    double* Q = L.mats[3];
+    double* T2 = L.mats[4];
+    double* W = L.mats[5];
+
+    // A0
+    const NS_GLOBAL double* gp = gbl(S.gram);
+    double av[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+        av[i] = 0.0;
+    for (int q = 0; q < S.nslices; q += 8) {
+        double t[8][EPT];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const int e = tid + kSmallThreads * i;
+                t[u][i] = (q + u < S.nslices && e < MM) ? gp[(size_t)(q + u) * MM + e] : 0.0;
+            }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < EPT; ++i)
+                if (q + u < S.nslices)
+                    av[i] += t[u][i];
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid + kSmallThreads * i;
+        if (e < MM)
+            A[e] = av[i];
+    }
+    const double inv = small_inv(S, L.red);   // (its barriers also publish A)
+
+    // the steps: B'_k = aI + b A_k + c A_k^2; Q <- B'_k Q; A <- A B'_k^2
+    for (int k = 0; k < steps; ++k) {
+        const float* c3 = co.v + (co.per_step ? 3 * k : 0);
+        const double ca = c3[0], cb = c3[1], cc = c3[2];
+        small_mm<MR>(A, A, Sq);
+        for (int e = tid; e < MM; e += kSmallThreads) {
+            const double v = cb * A[e] + cc * Sq[e];
+            P[e] = e / MR == e % MR ? v + ca : v;
+        }
+        __syncthreads();
+        if (k == 0) {
+            for (int e = tid; e < MM; e += kSmallThreads)
+                Q[e] = P[e];
+            __syncthreads();
+        } else {
+            small_mm<MR>(P, Q, W);
+            double* sw = Q; Q = W; W = sw;
+        }
+        if (k + 1 < steps) {
+            small_mm<MR>(P, P, T2);
+            small_mm<MR>(A, T2, W);
+            double* sw = A; A = W; W = sw;
+        }
+    }
+
+    // Y = Q X0 (Q's row i read as 16-byte pieces, the same address in every lane)
+    for (int64_t c = c0 + col; c < c1; c += CW) {
+        double x[MR];
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+            x[r] = r < m ? small_g<T>(S, r, c) * inv : 0.0;
+#pragma unroll 2
+        for (int r = 0; r < H; ++r) {
+            const int row = r0 + r;
+            double y0 = 0.0, y1 = 0.0;
+#pragma unroll
+            for (int t = 0; t < MR; t += 2) {
+                const double2 q2 = *reinterpret_cast<const double2*>(Q + row * MR + t);
+                y0 = fma(q2.x, x[t], y0);
+                y1 = fma(q2.y, x[t + 1], y1);
+            }
+            if (row < m)
+                small_put<T>(S, row, c, y0 + y1);
         }
     }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kSmallThreads) void k_small(const SmallMat* __restrict__ mats, int steps,
-                                                    const CoeffTable coeffs, int xl_floats)
+// Phases [p0, p1) of one slice, in order. A matrix of one slice runs every
+// phase in the launch of phase 0 (the same code in the same order, so the
+// same bits) and its workgroup returns at once in the later launches;
+// between the phases its pieces pass through global memory within the
+// workgroup, ordered by __syncthreads.
+template <int DT, int MR, int RG>
+__device__ __forceinline__ void small_phases(const SmallMat& S, int slice, int p0, int p1, int steps,
+                                             const SmallCoeffs& co, SmallLds& L)
 {
-    extern __shared__ float lds[];
-    const SmallMat S = mats[blockIdx.x];
-    const int mr = (S.m + 7) & ~7;
-    // X resident in LDS when its n x (MR + 4) floats fit the launch's share
-    const bool xl = (int64_t)S.n * (mr + 4) <= xl_floats;
-    switch (mr) {
-    case 8:
-        xl ? small_body<DT, 8, true>(S, steps, coeffs, lds) : small_body<DT, 8, false>(S, steps, coeffs, lds);
-        break;
-    case 16:
-        xl ? small_body<DT, 16, true>(S, steps, coeffs, lds) : small_body<DT, 16, false>(S, steps, coeffs, lds);
-        break;
-    case 24:
-        xl ? small_body<DT, 24, true>(S, steps, coeffs, lds) : small_body<DT, 24, false>(S, steps, coeffs, lds);
-        break;
-    default:
-        xl ? small_body<DT, 32, true>(S, steps, coeffs, lds) : small_body<DT, 32, false>(S, steps, coeffs, lds);
-        break;
+    for (int ph = p0; ph < p1; ++ph) {
+        if (ph > p0)
+            __syncthreads();
+        if (ph == 0)
+            small_norm_piece<DT, MR, RG>(S, slice, L);
+        else if (ph == 1)
+            small_gram_piece<DT, MR>(S, slice, steps == 0, L);
+        else
+            small_finish<DT, MR, RG>(S, slice, steps, co, L);
     }
+}
+
+// One launch covers the small matrices of one MR (the planner groups them);
+// workgroup b (counted from prefix[0]) is slice b - prefix[i] of matrix i.
+template <int DT, int MR>
+__global__ __launch_bounds__(kSmallThreads) void k_small(const SmallMat* __restrict__ mats, int nmats,
+                                                         const int32_t* __restrict__ prefix, int phase,
+                                                         int steps, const SmallCoeffs co)
+{
+    __shared__ __attribute__((aligned(16))) SmallLds L;
+    const int b = prefix[0] + (int)blockIdx.x;
+    const int mi = find_mat(prefix, nmats, b);
+    const SmallMat& S = mats[mi];
+    const int slice = b - prefix[mi];
+    const int last = steps > 0 ? 2 : 1;   // the last phase
+    int p0 = phase, p1 = phase + 1;
+    if (S.nslices == 1)
+        p1 = phase == 0 ? last + 1 : phase;
+    if (S.n <= kSmallThreads / 2)   // two threads per column
+        small_phases<DT, MR, 2>(S, slice, p0, p1, steps, co, L);
+    else
+        small_phases<DT, MR, 1>(S, slice, p0, p1, steps, co, L);
 }
 
 // Norm, pass 1: one workgroup per kNormChunk-element piece of a matrix (in its
@@ -1804,47 +1920,33 @@ hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, in
 }
 }  // namespace
 
-int small_lds_floats(int max_xl_floats)
+template <int DT, int MR>
+hipError_t launch_small_t(const SmallMat* mats, int count, const int32_t* slice_prefix, int nslices, int phase,
+                          int steps, const SmallCoeffs& co, hipStream_t stream)
 {
-    const int x_area = max_xl_floats > kSmallChunk * 36 ? max_xl_floats : kSmallChunk * 36;
-    return kSmallPartFloats + kSmallSqFloats + 8 + x_area;
-}
-
-int small_xl_floats(int m, int n)
-{
-    const int64_t need = (int64_t)n * (((m + 7) & ~7) + 4);
-    return need <= kSmallXlMaxFloats ? (int)need : 0;
-}
-
-hipError_t launch_small(int dtype, const SmallMat* mats, int count, int steps,
-                        const CoeffTable& coeffs, int xl_floats, hipStream_t stream)
-{
-    const size_t lds = sizeof(float) * (size_t)small_lds_floats(xl_floats);
-    // Allow the kernel its largest dynamic LDS once per device and dtype
-    // (above the 64 KB default).
-    static std::mutex mu;
-    static std::set<std::pair<int, int>> done;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return e;
-    {
-        std::lock_guard<std::mutex> lk(mu);
-        if (!done.count({dev, dtype})) {
-            const int max_lds = (int)(sizeof(float) * (size_t)small_lds_floats(kSmallXlMaxFloats));
-            e = dtype == 0
-                ? hipFuncSetAttribute((const void*)k_small<0>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds)
-                : hipFuncSetAttribute((const void*)k_small<1>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-            if (e != hipSuccess)
-                return e;
-            done.insert({dev, dtype});
-        }
-    }
-    if (dtype == 0)
-        hipLaunchKernelGGL(k_small<0>, dim3(count), dim3(kSmallThreads), lds, stream, mats, steps, coeffs, xl_floats);
-    else
-        hipLaunchKernelGGL(k_small<1>, dim3(count), dim3(kSmallThreads), lds, stream, mats, steps, coeffs, xl_floats);
+    hipLaunchKernelGGL((k_small<DT, MR>), dim3(nslices), dim3(kSmallThreads), 0, stream, mats, count, slice_prefix,
+                       phase, steps, co);
     return hipGetLastError();
+}
+
+hipError_t launch_small(int dtype, int mr, const SmallMat* mats, int count, const int32_t* slice_prefix,
+                        int nslices, int phase, int steps, const SmallCoeffs& co, hipStream_t stream)
+{
+    switch (mr) {
+    case 8:
+        return dtype == 0 ? launch_small_t<0, 8>(mats, count, slice_prefix, nslices, phase, steps, co, stream)
+                          : launch_small_t<1, 8>(mats, count, slice_prefix, nslices, phase, steps, co, stream);
+    case 16:
+        return dtype == 0 ? launch_small_t<0, 16>(mats, count, slice_prefix, nslices, phase, steps, co, stream)
+                          : launch_small_t<1, 16>(mats, count, slice_prefix, nslices, phase, steps, co, stream);
+    case 24:
+        return dtype == 0 ? launch_small_t<0, 24>(mats, count, slice_prefix, nslices, phase, steps, co, stream)
+                          : launch_small_t<1, 24>(mats, count, slice_prefix, nslices, phase, steps, co, stream);
+    case 32:
+        return dtype == 0 ? launch_small_t<0, 32>(mats, count, slice_prefix, nslices, phase, steps, co, stream)
+                          : launch_small_t<1, 32>(mats, count, slice_prefix, nslices, phase, steps, co, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_norm_partial(int dtype, const LargeMat* mats, int nmats, const int32_t* part_prefix,

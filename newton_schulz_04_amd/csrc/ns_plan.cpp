@@ -235,7 +235,12 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
     }
     auto by_cost = [&](int32_t a, int32_t b) { return p.mats[a].cost > p.mats[b].cost; };
     std::stable_sort(p.large.begin(), p.large.end(), by_cost);
-    std::stable_sort(p.small.begin(), p.small.end(), by_cost);
+    // small matrices: grouped by m rounded up to 8 (one kernel instance per
+    // group), largest cost first within a group
+    std::stable_sort(p.small.begin(), p.small.end(), [&](int32_t a, int32_t b) {
+        const int ra = (p.mats[a].m + 7) / 8, rb = (p.mats[b].m + 7) / 8;
+        return ra != rb ? ra < rb : p.mats[a].cost > p.mats[b].cost;
+    });
 
     // Tile lists. Norm and normalize pieces per matrix first.
     p.part_prefix.assign(1, 0);
@@ -303,11 +308,27 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
         }
         p.large_off.push_back(lo);
     }
+    p.small_prefix.assign(1, 0);
     for (int32_t idx : p.small) {
         const PlanMat& pm = p.mats[idx];
-        p.small_off.push_back(off);
-        off = align_up(off + 4 * (size_t)pm.m * pm.n);
+        SmallOffsets so{};
+        so.mr = (pm.m + 7) / 8 * 8;
+        const int64_t chunks = ((int64_t)pm.n + kSmallSlice - 1) / kSmallSlice;
+        const int64_t per = (chunks + kSmallMaxSlices - 1) / kSmallMaxSlices;   // chunks per slice
+        so.slice_cols = (int32_t)(per * kSmallSlice);
+        so.nslices = (int32_t)((pm.n + so.slice_cols - 1) / so.slice_cols);
+        if ((int64_t)p.small_prefix.back() + so.nslices > std::numeric_limits<int32_t>::max()) {
+            *err = "batch too large";
+            return 1;
+        }
+        p.small_prefix.push_back(p.small_prefix.back() + so.nslices);
+        so.gram = off;
+        off = align_up(off + 8 * (size_t)so.nslices * so.mr * so.mr);
+        so.norm = off;
+        off = align_up(off + 8 * (size_t)so.nslices);
+        p.small_off.push_back(so);
     }
+    p.total_small = p.small_prefix.back();
     p.data_bytes = off;
     // Metadata lives in its own allocation, laid out from 0.
     off = 0;
@@ -325,6 +346,8 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
     off = align_up(off + sizeof(int32_t) * p.part_prefix.size());
     p.meta_prep_prefix = off;
     off = align_up(off + sizeof(int32_t) * p.prep_prefix.size());
+    p.meta_small_prefix = off;
+    off = align_up(off + sizeof(int32_t) * p.small_prefix.size());
     p.meta_inv = off;   // (scale, 2^E) per matrix
     off = align_up(off + 2 * sizeof(float) * p.large.size());
     p.meta_partials = off;   // scaled sums, then exponents, per piece

@@ -30,6 +30,10 @@ struct PlanMat {
 struct LargeOffsets {
     size_t xlo, xb[2], xt[2], a, b, adiag, bdiag;
 };
+struct SmallOffsets {
+    size_t gram, norm;
+    int32_t mr, nslices, slice_cols;
+};
 
 struct Plan {
     int dtype = 0;                       // ns_dtype
@@ -38,7 +42,9 @@ struct Plan {
     std::vector<int32_t> large;          // batch indices, launch order
     std::vector<int32_t> small;          // batch indices, launch order
     std::vector<LargeOffsets> large_off; // parallel to `large`
-    std::vector<size_t> small_off;       // parallel to `small`
+    std::vector<SmallOffsets> small_off; // parallel to `small`
+    std::vector<int32_t> small_prefix;   // slices (workgroups) per small matrix, prefix, size nsmall+1
+    int32_t total_small = 0;
     std::vector<Tile> syrk_tiles;        // stage XX^T   (upper tiles, K = np)
     std::vector<Tile> poly_tiles;        // stage bA+cA^2 (upper tiles, K = mp)
     std::vector<Tile> update_tiles;      // stage aX+BX  (all tiles,   K = mp)
@@ -56,7 +62,7 @@ struct Plan {
     // lists (uploaded, [0, meta_inv)) and per-call scalars (inv, partials).
     size_t data_bytes = 0;
     size_t meta_large = 0, meta_small = 0, meta_syrk = 0, meta_poly = 0, meta_update = 0,
-           meta_part_prefix = 0, meta_prep_prefix = 0, meta_inv = 0,
+           meta_part_prefix = 0, meta_prep_prefix = 0, meta_small_prefix = 0, meta_inv = 0,
            meta_partials = 0, meta_end = 0;
     size_t total_bytes() const { return data_bytes + meta_end; }
 };

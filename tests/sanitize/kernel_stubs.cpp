@@ -6,8 +6,8 @@
 
 namespace ns {
 
-int small_xl_floats(int, int) { return 0; }
-hipError_t launch_small(int, const SmallMat*, int, int, const CoeffTable&, int, hipStream_t)
+hipError_t launch_small(int, int, const SmallMat*, int, const int32_t*, int, int, int, const SmallCoeffs&,
+                        hipStream_t)
 {
     return hipErrorNotSupported;
 }

@@ -166,3 +166,15 @@ def test_norm_scaling_keeps_ordinary_inputs_bitwise():
     h[0, 0] = 2.0 ** 39
     (y,) = gpu_run([h])
     assert rel_err(y, oracle_run(h)) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("shape", [(20, 300), (300, 20), (40, 300)])
+def test_more_steps_than_a_schedule_holds(shape):
+    # the plain call takes any step count (a schedule holds at most 64):
+    # 70 cubic steps converge to the polar factor on both size classes
+    g = workloads.gaussian(shape, seed=66, index=shape[0], dtype=torch.float32)
+    cubic = (1.5, -0.5, 0.0)
+    (y,) = gpu_run([g], steps=70, coeffs=cubic)
+    assert rel_err(y, oracle_run(g, steps=70, coeffs=cubic)) <= TOL[torch.float32]
+    u, _, vt = np.linalg.svd(g.double().numpy(), full_matrices=False)
+    assert rel_err(y, u @ vt) <= TOL[torch.float32]
