@@ -215,7 +215,8 @@ def summary_md(stats_csv, traffic_json, bench_json, title, shapes, kt_command, m
 The bf16 MFMA peak assumes 2.4 GHz; the shader clock under this load is what
 the power limit leaves. syrk and poly compute only the upper-triangle tiles
 (300 of 576 per 6144 x 6144 output), so their metric TFLOP/s count about
-twice the MFMA work they do.
+twice the MFMA work they do; bench.py reports `tflops_tiles` (what the MFMAs
+execute) beside it.
 """
     cp = t["copy_probe"]
     return f"""# {title}
@@ -226,15 +227,18 @@ bA + cA^2, update = `k_gemm<0, 2, 0, 0>` aX + BX; the fifth update is `k_gemm<0,
 which writes the caller's buffer; syrk_half and poly_half = `k_gemm<0, 0|1, 0, 1>`
 run the half tiles of a split last round, a second launch of the stage, and
 count with it in the traffic table). `copy_probe` rows are the runtime's
-device copies (bench restores its inputs between steps, outside the timed region).
+device copies (bench restores its inputs from a pristine copy before the timed
+pass and before the profiling pass, outside both).
 Run from the repository root with `export TMPDIR=/tmp` and the library built
 in-tree (`python -c "import __graft_entry__ as g; g.build()"`).
 
 ## Kernel trace (rocprofv3 --kernel-trace --stats)
 
 {stats_md(stats_csv, kt_command)}
-The same run's bench line (HIP events on the launch stream): value {b['value']}
-matrices/s, {b['tflops']} TFLOP/s ({b['pct_bf16_peak']}% of 2.5 PFLOP/s); per-launch ms:
+The same run's bench line: value {b['value']} matrices/s (timed pass, no events),
+{b['tflops']} TFLOP/s ({b['pct_bf16_peak']}% of 2.5 PFLOP/s, the metric's 4m^2n + 2m^3
+convention; executed by the kernels: {b.get('executed', {}).get('tiles_tflops')} TFLOP/s); per-launch ms from
+HIP events on the launch stream in bench.py's separate profiling pass:
 {", ".join(f"{k} {v}" for k, v in ks.items())}.
 
 ## HBM-side traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
