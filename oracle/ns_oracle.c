@@ -11,9 +11,10 @@
  * shards"), Fix section, orthogonalizes each assembled 2-D update matrix with
  * Newton-Schulz and notes that zero rows stay zero; NVIDIA/Megatron-LM PR #6379
  * ("Balance LayerWise optimizer shards by Newton-Schulz cost"), Changes item 1,
- * gives its cost as max(M,N)*min(M,N)^2. The iteration itself is Muon's
- * quintic Newton-Schulz map (K. Jordan et al., "Muon: An optimizer for hidden
- * layers in neural networks", 2024), which this library adopts as its contract:
+ * gives its cost as max(M,N)*min(M,N)^2. The pages give neither the
+ * normalization nor the coefficients; the specification this oracle checks
+ * the library against fixes the iteration, eps, the orientation, 5 steps and
+ * the quintic coefficients:
  *
  *   X = G / (||G||_F + eps)                      eps = 1e-7 by default
  *   if rows > cols:  X = X^T                     (so X is m x n with m <= n)

@@ -178,3 +178,17 @@ def test_more_steps_than_a_schedule_holds(shape):
     assert rel_err(y, oracle_run(g, steps=70, coeffs=cubic)) <= TOL[torch.float32]
     u, _, vt = np.linalg.svd(g.double().numpy(), full_matrices=False)
     assert rel_err(y, u @ vt) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("dtype,shape", [(torch.bfloat16, (8, 200000)), (torch.float32, (150000, 20))])
+def test_small_path_wide_slices(dtype, shape):
+    # n > 131072: a small matrix's columns go into slices of 1024 (at most
+    # 256 slices), each workgroup looping over several 512- and 256-column
+    # chunks; against the oracle, and bitwise the same inside a batch
+    g = workloads.gaussian(shape, seed=67, index=shape[0], dtype=dtype)
+    (y,) = gpu_run([g])
+    assert rel_err(y, oracle_run(g)) <= TOL[dtype]
+    other = workloads.gaussian((16, 300), seed=67, index=1, dtype=dtype)
+    y2, _ = gpu_run([g, other])
+    iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(y.view(iv), y2.view(iv))
