@@ -232,7 +232,7 @@ struct SmallLds {
             double xs[kSmallChunk * kSmallPx];   // a chunk of X0's columns
             double part[kSmallPartDoubles];      // Gram pieces per column group
         } g;
-        double mats[6][32 * 32];                 // the m x m matrices, pitch MR
+        double mats[6][32 * 32];                 // the m x m matrices, 32 x 32, zero-padded
     };
     double red[kSmallWaves];
 };
@@ -396,30 +396,31 @@ __device__ __forceinline__ void small_gram_piece(const SmallMat& S, int slice, b
     }
 }
 
-// Z = X^T Y for MR x MR matrices in LDS (pitch MR): with X symmetric, X Y.
-// Thread t < (MR / 2)^2 computes the 2 x 2 block (2 (t / (MR / 2)),
-// 2 (t mod (MR / 2))): each element sums X[k][i] Y[k][j] over k, even and odd
-// k apart, then their sum.
-template <int MR>
+// Z = X^T Y for 32 x 32 matrices in LDS (row-major, zero outside the m x m
+// corner but for the identity parts of B', which keep every product
+// block-diagonal): with X symmetric, X Y. fp64 MFMA 16 x 16 x 4: wavefront
+// w < 4 computes output block (w >> 1, w & 1), eight MFMAs over k. Lane l's
+// operands are a = X^T[16 bi + l % 16][4 kb + l / 16] = X[4 kb + l / 16][16 bi
+// + l % 16] and b = Y[4 kb + l / 16][16 bj + l % 16] (both rows read across 16
+// lanes); accumulator register r of lane l is Z[16 bi + 4 r + l / 16][16 bj +
+// l % 16] (lane layout checked with an in-bounds probe on gfx950).
+constexpr int kMx = 32;
+typedef double d4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void small_mm(const double* X, const double* Y, double* Z)
 {
-    constexpr int NB = MR / 2;
-    const int t = threadIdx.x;
-    if (t < NB * NB) {
-        const int i0 = 2 * (t / NB), j0 = 2 * (t % NB);
-        double z[2][2][2] = {};
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+    if (wave < 4) {
+        const int bi = wave >> 1, bj = wave & 1, kl = l >> 4, il = l & 15;
+        d4 c = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int k = 0; k < MR; ++k) {
-            const double2 xa = *reinterpret_cast<const double2*>(X + k * MR + i0);
-            const double2 yb = *reinterpret_cast<const double2*>(Y + k * MR + j0);
-            z[k & 1][0][0] = fma(xa.x, yb.x, z[k & 1][0][0]);
-            z[k & 1][0][1] = fma(xa.x, yb.y, z[k & 1][0][1]);
-            z[k & 1][1][0] = fma(xa.y, yb.x, z[k & 1][1][0]);
-            z[k & 1][1][1] = fma(xa.y, yb.y, z[k & 1][1][1]);
+        for (int kb = 0; kb < kMx / 4; ++kb) {
+            const double a = X[(4 * kb + kl) * kMx + 16 * bi + il];
+            const double b = Y[(4 * kb + kl) * kMx + 16 * bj + il];
+            c = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
         }
-        *reinterpret_cast<double2*>(Z + i0 * MR + j0) = make_double2(z[0][0][0] + z[1][0][0], z[0][0][1] + z[1][0][1]);
-        *reinterpret_cast<double2*>(Z + (i0 + 1) * MR + j0) =
-            make_double2(z[0][1][0] + z[1][1][0], z[0][1][1] + z[1][1][1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Z[(16 * bi + 4 * r + kl) * kMx + 16 * bj + il] = c[r];
     }
     __syncthreads();
 }
@@ -434,7 +435,6 @@ __device__ __forceinline__ void small_finish(const SmallMat& S, int slice, int s
 {
     using T = typename Elt<DT>::type;
     constexpr int MM = MR * MR, H = MR / RG, CW = kSmallThreads / RG;
-    constexpr int EPT = (MM + kSmallThreads - 1) / kSmallThreads;
     const int tid = threadIdx.x, col = tid % CW, r0 = (tid / CW) * H;
     const int m = S.m;
     const int64_t c0 = (int64_t)slice * S.slice_cols;
@@ -446,57 +446,57 @@ __device__ __forceinline__ void small_finish(const SmallMat& S, int slice, int s
     double* T2 = L.mats[4];
     double* W = L.mats[5];
 
-    // A0
+    // A0 (32 x 32, zero outside the MR x MR pieces)
     const NS_GLOBAL double* gp = gbl(S.gram);
-    double av[EPT];
+    constexpr int EPX = kMx * kMx / kSmallThreads;
+    double av[EPX];
 #pragma unroll
-    for (int i = 0; i < EPT; ++i)
+    for (int i = 0; i < EPX; ++i)
         av[i] = 0.0;
     for (int q = 0; q < S.nslices; q += 8) {
-        double t[8][EPT];
+        double t[8][EPX];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const int e = tid + kSmallThreads * i;
-                t[u][i] = (q + u < S.nslices && e < MM) ? gp[(size_t)(q + u) * MM + e] : 0.0;
+            for (int i = 0; i < EPX; ++i) {
+                const int x = tid + kSmallThreads * i, r = x / kMx, c = x % kMx;
+                t[u][i] = (q + u < S.nslices && r < MR && c < MR) ? gp[(size_t)(q + u) * MM + r * MR + c] : 0.0;
             }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int i = 0; i < EPT; ++i)
+            for (int i = 0; i < EPX; ++i)
                 if (q + u < S.nslices)
                     av[i] += t[u][i];
     }
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int e = tid + kSmallThreads * i;
-        if (e < MM)
-            A[e] = av[i];
-    }
+    for (int i = 0; i < EPX; ++i)
+        A[tid + kSmallThreads * i] = av[i];
     const double inv = small_inv(S, L.red);   // (its barriers also publish A)
 
     // the steps: B'_k = aI + b A_k + c A_k^2; Q <- B'_k Q; A <- A B'_k^2
+    // (the padding rows and columns only ever meet the identity: every
+    // product stays zero outside the m x m corner but on the diagonal)
     for (int k = 0; k < steps; ++k) {
         const float* c3 = co.v + (co.per_step ? 3 * k : 0);
         const double ca = c3[0], cb = c3[1], cc = c3[2];
-        small_mm<MR>(A, A, Sq);
-        for (int e = tid; e < MM; e += kSmallThreads) {
+        small_mm(A, A, Sq);
+        for (int e = tid; e < kMx * kMx; e += kSmallThreads) {
             const double v = cb * A[e] + cc * Sq[e];
-            P[e] = e / MR == e % MR ? v + ca : v;
+            P[e] = e / kMx == e % kMx ? v + ca : v;
         }
         __syncthreads();
         if (k == 0) {
-            for (int e = tid; e < MM; e += kSmallThreads)
+            for (int e = tid; e < kMx * kMx; e += kSmallThreads)
                 Q[e] = P[e];
             __syncthreads();
         } else {
-            small_mm<MR>(P, Q, W);
+            small_mm(P, Q, W);
             double* sw = Q; Q = W; W = sw;
         }
         if (k + 1 < steps) {
-            small_mm<MR>(P, P, T2);
-            small_mm<MR>(A, T2, W);
+            small_mm(P, P, T2);
+            small_mm(A, T2, W);
             double* sw = A; A = W; W = sw;
         }
     }
@@ -513,7 +513,7 @@ __device__ __forceinline__ void small_finish(const SmallMat& S, int slice, int s
             double y0 = 0.0, y1 = 0.0;
 #pragma unroll
             for (int t = 0; t < MR; t += 2) {
-                const double2 q2 = *reinterpret_cast<const double2*>(Q + row * MR + t);
+                const double2 q2 = *reinterpret_cast<const double2*>(Q + row * kMx + t);
                 y0 = fma(q2.x, x[t], y0);
                 y1 = fma(q2.y, x[t + 1], y1);
             }
