@@ -187,6 +187,41 @@ def metric_flops_per_kind(shapes):
     return f, a
 
 
+def accuracy_vs_stored_oracle(workload, mats_cpu, outputs):
+    """Relative error of this run's results against the stored fp64 oracle
+    samples of the workload (tests/golden/oracle_<workload>_<i>.npz, written
+    by tests/golden/make_oracle_golden.py): per sampled matrix, over its
+    stored rows and columns. Only the data files are read; None when the
+    workload has no stored sample or an input's hash differs."""
+    import numpy as np
+    from newton_schulz_04_amd import workloads as wl
+    base = {"dense_lowrank": "dense_lowrank"}.get(workload)
+    if workload.startswith("ragged_remainder_"):
+        base = "ragged_remainder"
+    if base is None or mats_cpu is None:
+        return None
+    out = {}
+    for i, (g, y) in enumerate(zip(mats_cpu, outputs)):
+        path = os.path.join(ROOT, "tests", "golden", f"oracle_{base}_{i}.npz")
+        if not os.path.exists(path):
+            continue
+        with np.load(path, allow_pickle=False) as z:
+            if str(z["input_sha256"]) != wl.sha256(g):
+                continue
+            yf = y.float().cpu().numpy().astype(np.float64)
+            rows, ref = z["rows_idx"], z["rows"].astype(np.float64)
+            num, den = np.linalg.norm(yf[rows] - ref) ** 2, np.linalg.norm(ref) ** 2
+            if "cols_idx" in z.files:
+                cols, refc = z["cols_idx"], z["cols"].astype(np.float64)
+                num += np.linalg.norm(yf[:, cols] - refc) ** 2
+                den += np.linalg.norm(refc) ** 2
+            out[f"matrix_{i}"] = float(np.sqrt(num / den))
+    if not out:
+        return None
+    return {"max_rel_err": max(out.values()), "per_matrix": out,
+            "against": "stored fp64 oracle rows and columns (tests/golden)", "tolerance": 2e-2}
+
+
 def measured_traffic(workload, kind):
     """HBM bytes per launch of `kind` from the committed PMC summary of this
     workload, or None when there is none or the library sources changed since
@@ -243,6 +278,9 @@ def main():
     fp32 = all(m.dtype == torch.float32 for m in mats)
     elt = 4 if fp32 else 2
     cpu_mats = [m.clone() for m in mats] if small_batch else None
+    # CPU copies of the inputs the stored oracle samples cover
+    ref_inputs = [m.clone() for m in mats] if (args.workload == "dense_lowrank" or
+                                               args.workload.startswith("ragged_remainder_")) else None
     h = hashlib.sha256()
     for m in mats:
         h.update(m.cpu().contiguous().view(torch.uint8).numpy().tobytes())
@@ -361,6 +399,9 @@ def main():
             "tiles_tflops": round(tiles_all / step_s / 1e12, 1),
             "tiles_pct_peak": round(100 * tiles_all / step_s / 1e12 / peak_main, 2),
         }
+    acc = accuracy_vs_stored_oracle(args.workload, ref_inputs, batches[args.steps - 1])
+    if acc is not None:
+        out["accuracy"] = acc
     if not args.no_cpu_baseline:
         try:
             log("timing the CPU oracle on a bounded sample")

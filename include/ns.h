@@ -46,7 +46,16 @@
  * Threading. Entry points may be called from several host threads; calls
  * that share a (device, stream) pair are serialized on a lock. All GPU work
  * is enqueued on the caller's stream and no entry point waits for the device,
- * except ns_profile_read and ns_release_workspace as documented.
+ * except ns_profile_read and ns_release_workspace as documented, and the
+ * NS_CHECK debug mode below.
+ *
+ * Environment (read at every call):
+ *   NS_SMALL_M=t  an integer 0..32: matrices with min(rows, cols) <= t take
+ *                 the small-matrix path (default 32); others the tiled path.
+ *                 Other values are ignored.
+ *   NS_CHECK=1    debug mode: the call waits for the stream after every
+ *                 kernel launch and returns NS_EHIP naming the first kernel
+ *                 that failed.
  */
 #ifndef NS_H
 #define NS_H

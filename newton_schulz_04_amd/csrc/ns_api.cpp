@@ -20,6 +20,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
 #include <map>
@@ -348,9 +349,10 @@ void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* m
 namespace {
 
 bool same_key(const CachedPlan& cp, const int64_t* shapes, const Layout& L, int32_t count,
-              int32_t dtype, void* ws)
+              int32_t dtype, void* ws, int32_t small_max)
 {
-    if (cp.dtype != dtype || cp.ws_base != ws || cp.shapes.size() != (size_t)count * 2)
+    if (cp.dtype != dtype || cp.ws_base != ws || cp.shapes.size() != (size_t)count * 2 ||
+        cp.plan->small_max != small_max)
         return false;
     if (std::memcmp(cp.shapes.data(), shapes, sizeof(int64_t) * 2 * count) != 0)
         return false;
@@ -370,10 +372,40 @@ bool same_key(const CachedPlan& cp, const int64_t* shapes, const Layout& L, int3
     return true;
 }
 
-// Launch helper: records profiling events around `fn` when profiling is on.
+// NS_CHECK=1 in the environment (read at every call): a debug mode that
+// waits for the stream after every launch and reports the first kernel that
+// failed, by kind. The one case in which an entry point waits for the device.
+bool check_mode()
+{
+    const char* v = std::getenv("NS_CHECK");
+    return v && v[0] == '1' && v[1] == 0;
+}
+
+const char* kind_name(int kind)
+{
+    static const char* names[ns::kNumKinds] = {"norm partial sums", "norm fold", "normalize", "X X^T",
+                                               "bA + cA^2", "aX + BX", "small-matrix", "steps == 0 write-back"};
+    return kind >= 0 && kind < ns::kNumKinds ? names[kind] : "unknown";
+}
+
+thread_local bool t_check = false;   // check_mode() of the current call
+thread_local std::string t_check_msg;
+
+// Launch helper: records profiling events around `fn` when profiling is on;
+// in NS_CHECK mode, waits for the stream after the launch.
 template <typename F>
 hipError_t timed(int kind, hipStream_t stream, F&& fn)
 {
+    if (t_check) {
+        hipError_t e = fn();
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(stream);
+        if (e == hipSuccess)
+            e = hipGetLastError();
+        if (e != hipSuccess)
+            t_check_msg = std::string("NS_CHECK: the ") + kind_name(kind) + " kernel failed";
+        return e;
+    }
     if (!g_prof_on.load(std::memory_order_relaxed))
         return fn();
     hipEvent_t a = prof_event(), b = prof_event();
@@ -393,8 +425,9 @@ ns_status run(Context* c, const int64_t* shapes, const Layout& L, int32_t count,
     hipStream_t stream = c->stream;
     // Plan (or reuse) --------------------------------------------------------
     CachedPlan* hit = nullptr;
+    const int32_t small_max = ns::small_threshold();
     for (CachedPlan& cp : c->plans)
-        if (same_key(cp, shapes, L, count, dtype, c->ws)) {
+        if (same_key(cp, shapes, L, count, dtype, c->ws, small_max)) {
             hit = &cp;
             break;
         }
@@ -466,6 +499,17 @@ namespace ns {
 
 ns_status enqueue(const Plan& p, char* meta, int32_t steps, const float* coeffs, int32_t per_step,
                   int32_t dtype, hipStream_t stream)
+{
+    t_check = check_mode();
+    t_check_msg.clear();
+    const ns_status st = enqueue_launches(p, meta, steps, coeffs, per_step, dtype, stream);
+    if (st == NS_EHIP && !t_check_msg.empty())
+        return fail(NS_EHIP, t_check_msg + " (" + ns_last_error() + ")");
+    return st;
+}
+
+ns_status enqueue_launches(const Plan& p, char* meta, int32_t steps, const float* coeffs, int32_t per_step,
+                           int32_t dtype, hipStream_t stream)
 {
     auto* large = reinterpret_cast<const ns::LargeMat*>(meta + p.meta_large);
     auto* small = reinterpret_cast<const ns::SmallMat*>(meta + p.meta_small);

@@ -46,8 +46,11 @@ void build_meta(const Plan& p, const Layout& L, int32_t count, char* ws, char* m
 
 // Enqueues the kernel sequence of a planned batch on `stream`: `meta` is the
 // device metadata block (uploaded image, then the device-written norm
-// scratch up to p.meta_end). Nothing is allocated and nothing waits.
+// scratch up to p.meta_end). Nothing is allocated and nothing waits (but in
+// the NS_CHECK=1 debug mode, which waits after every launch).
 ns_status enqueue(const Plan& p, char* meta, int32_t steps, const float* coeffs, int32_t per_step,
                   int32_t dtype, hipStream_t stream);
+ns_status enqueue_launches(const Plan& p, char* meta, int32_t steps, const float* coeffs, int32_t per_step,
+                           int32_t dtype, hipStream_t stream);
 
 }  // namespace ns

@@ -9,7 +9,8 @@ namespace ns {
 
 // Macro tile of the grouped MFMA GEMMs: 256 x 256 outputs per workgroup.
 constexpr int kTile = 256;
-// Matrices with min(rows, cols) <= kSmallMax run the fused one-workgroup
+// Matrices with min(rows, cols) <= kSmallMax (or the NS_SMALL_M environment
+// variable's lower threshold, see small_threshold) run the small-matrix
 // kernel in fp32.
 constexpr int kSmallMax = 32;
 // Elements per workgroup in the norm's partial-sum pass.

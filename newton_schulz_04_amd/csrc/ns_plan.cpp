@@ -13,6 +13,7 @@
 #include "ns_plan.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <limits>
 
 namespace ns {
@@ -160,6 +161,16 @@ std::vector<Tile> run_list(const std::vector<Tile>& tl, int32_t split)
 
 }  // namespace
 
+int32_t small_threshold()
+{
+    const char* v = std::getenv("NS_SMALL_M");
+    if (!v || !*v)
+        return kSmallMax;
+    char* end = nullptr;
+    const long t = std::strtol(v, &end, 10);
+    return (*end == 0 && t >= 0 && t <= kSmallMax) ? (int32_t)t : kSmallMax;
+}
+
 int64_t ns_cost(int64_t rows, int64_t cols)
 {
     if (rows < 0 || cols < 0)
@@ -188,6 +199,7 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
     Plan& p = *plan;
     p = Plan();
     p.dtype = dtype;
+    p.small_max = small_threshold();
     p.elt = dtype == 0 ? 2 : 4;
     p.mats.resize(count);
     for (int32_t i = 0; i < count; ++i) {
@@ -210,7 +222,7 @@ int make_plan(const int64_t* shapes, int32_t count, int32_t dtype, Plan* plan, s
         pm.cost = ns_cost(rows, cols);
         if (rows == 0 || cols == 0) {
             pm.cls = kEmpty;
-        } else if (pm.m <= kSmallMax) {
+        } else if (pm.m <= p.small_max) {
             pm.cls = kSmall;
         } else {
             pm.cls = kLarge;

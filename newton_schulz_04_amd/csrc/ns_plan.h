@@ -17,6 +17,11 @@ enum MatClass : int32_t { kEmpty = 0, kSmall = 1, kLarge = 2 };
 // max(M,N) * min(M,N)^2 (the Megatron-LM page's Newton-Schulz cost).
 int64_t ns_cost(int64_t rows, int64_t cols);
 
+// Largest min(rows, cols) of the small-matrix path: kSmallMax, or the value
+// of the environment variable NS_SMALL_M when it holds an integer in
+// [0, kSmallMax] (other values are ignored). Read at every planning.
+int32_t small_threshold();
+
 struct PlanMat {
     int32_t index;          // position in the caller's batch
     int64_t rows, cols;
@@ -37,6 +42,7 @@ struct SmallOffsets {
 
 struct Plan {
     int dtype = 0;                       // ns_dtype
+    int32_t small_max = kSmallMax;       // small-path threshold the plan was made with
     size_t elt = 2;                      // operand element bytes
     std::vector<PlanMat> mats;           // one per input, batch order
     std::vector<int32_t> large;          // batch indices, launch order

@@ -38,11 +38,16 @@ XCDS = 8
 SIMDS_PER_CU = 4
 
 
+# The sources whose changes can change what the counters measure: the
+# kernels, and the planner that orders their tiles and lays out the workspace.
+TRAFFIC_SOURCES = ("ns_kernels.hip", "ns_internal.h", "ns_plan.cpp", "ns_plan.h")
+
+
 def source_hash():
-    """sha256 over the library's sources (kernels, planner, launch code)."""
+    """sha256 over the kernel and planner sources (TRAFFIC_SOURCES)."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if os.path.splitext(path)[1] in (".hip", ".cpp", ".h"):
+        if os.path.basename(path) in TRAFFIC_SOURCES:
             h.update(os.path.basename(path).encode())
             with open(path, "rb") as f:
                 h.update(f.read())

@@ -277,3 +277,18 @@ def test_noalloc_validation_without_device():
     assert ns.orthogonalize_raw([fake + 1], [(300, 520)], 5, q, ns.NS_BF16, noalloc=True) == 1
     assert ns.orthogonalize_raw([0], [(0, 520)], 5, q, ns.NS_BF16, noalloc=True) == 0
     assert ns.orthogonalize_raw([fake], [(1 << 25, 4)], 5, q, ns.NS_BF16, noalloc=True) == 1
+
+
+def test_small_threshold_from_environment(monkeypatch):
+    # NS_SMALL_M lowers the small-path threshold (0..32); other values are
+    # ignored
+    shapes = [(24, 300), (33, 300), (8, 100), (300, 16)]
+    monkeypatch.delenv("NS_SMALL_M", raising=False)
+    assert ns.plan_classify(shapes, ns.NS_BF16) == [1, 2, 1, 1]
+    monkeypatch.setenv("NS_SMALL_M", "16")
+    assert ns.plan_classify(shapes, ns.NS_BF16) == [2, 2, 1, 1]
+    monkeypatch.setenv("NS_SMALL_M", "0")
+    assert ns.plan_classify(shapes, ns.NS_FP32) == [2, 2, 2, 2]
+    for bad in ("40", "-1", "x", "16x", ""):
+        monkeypatch.setenv("NS_SMALL_M", bad)
+        assert ns.plan_classify(shapes, ns.NS_BF16) == [1, 2, 1, 1], bad

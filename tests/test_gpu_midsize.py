@@ -192,3 +192,22 @@ def test_small_path_wide_slices(dtype, shape):
     y2, _ = gpu_run([g, other])
     iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
     assert torch.equal(y.view(iv), y2.view(iv))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_small_threshold_and_check_mode_from_environment(monkeypatch, dtype):
+    # the same 24 x 300 matrix on the small path (default) and, with
+    # NS_SMALL_M=8, on the tiled path: both against the oracle; NS_CHECK=1
+    # (wait and check after every launch) gives the same bits
+    g = workloads.gaussian((24, 300), seed=68, dtype=dtype)
+    ref = oracle_run(g)
+    monkeypatch.delenv("NS_SMALL_M", raising=False)
+    monkeypatch.delenv("NS_CHECK", raising=False)
+    (small,) = gpu_run([g])
+    monkeypatch.setenv("NS_SMALL_M", "8")
+    (tiled,) = gpu_run([g])
+    monkeypatch.setenv("NS_CHECK", "1")
+    (checked,) = gpu_run([g])
+    assert rel_err(small, ref) <= TOL[dtype] and rel_err(tiled, ref) <= TOL[dtype]
+    iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(tiled.view(iv), checked.view(iv))
