@@ -59,3 +59,48 @@ def test_calls_return_while_the_stream_is_busy():
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     ns.release_workspace(stream)
+
+
+def test_host_threads_on_their_own_streams():
+    # Entry points may be called from several host threads: four threads,
+    # each with its own stream (so its own workspace and plan cache), run
+    # mixed batches concurrently; every result equals the one-thread result
+    import threading
+    batches = []
+    for t in range(4):
+        shapes = [(300, 520), (24, 700), (520, 300 + 8 * t), (40, 2304)]
+        batches.append([workloads.gaussian(s, seed=73, index=10 * t + i) for i, s in enumerate(shapes)])
+    expect = []
+    for b in batches:
+        dev = [g.cuda() for g in b]
+        ns.orthogonalize(dev)
+        torch.cuda.synchronize()
+        expect.append([d.cpu() for d in dev])
+    results = [None] * 4
+    errors = []
+
+    def work(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                out = []
+                for _ in range(3):
+                    dev = [g.to("cuda", non_blocking=False) for g in batches[t]]
+                    ns.orthogonalize(dev, stream=s)
+                    out = dev
+                s.synchronize()
+                results[t] = [d.cpu() for d in out]
+            ns.release_workspace(s)
+        except Exception as e:  # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    for got, want in zip(results, expect):
+        assert got is not None
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
