@@ -12,8 +12,10 @@ pool's 8192x6144 matrices, the last one passed through 64 row shards),
 dense_lowrank_fp32 (the default's matrices through the fp32 path, fp32 MFMA),
 moe_mixed (130 matrices of four shapes), attn_gate (32 x 18x2304 passed as 8
 padded row shards each) and tiny_fp32 (4 x 64x32 fp32). The last two run in
-the fused small-matrix kernel: fp32 arithmetic on the vector ALUs, reported
-against the fp32 vector peak.
+the small-matrix kernel, which evaluates the iteration through the m x m Gram
+matrix in fp64 (vector FMAs for the Gram matrix and the final product, fp64
+MFMAs for the m x m steps); its roofline is taken against the 78.6 TFLOP/s
+fp64 peak.
 
 Prints one JSON line. `value` is matrices per second with the inputs already
 resident in HBM. Every timed step works on its own resident copy of the batch
@@ -21,6 +23,13 @@ resident in HBM. Every timed step works on its own resident copy of the batch
 reuses an output. The timed pass runs without the library's profiling events;
 per-kernel times (`kernels`, `roofline`) come from a separate pass of
 min(steps, 5) calls on fresh copies.
+
+`gpu_clock`: the graphics clock of each XCD and the socket power as the AMD
+SMI library reports them (the firmware's gpu_metrics table, refreshed every
+few hundred ms), sampled by a host thread through the warm-up and timed
+passes; the medians over the samples taken in the timed pass, the power cap,
+and the dominant kernel's roofline fraction against the peak scaled to that
+clock. Null where the library or the device is not available.
 
 FLOP conventions, reported side by side:
   tflops / pct_bf16_peak        the metric's convention, 5 (4 m^2 n + 2 m^3)
@@ -44,8 +53,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NS-orthogonalized matrices/s + TFLOP/s (% bf16 MFMA peak), 8192x6144 bf16"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector (the fused small-matrix kernel)
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 MFMA (the fp32 tiled path)
+PEAK_FP64_TFLOPS = 78.6   # MI355X fp64, vector and MFMA alike (the small-matrix path)
+PEAK_CLOCK_MHZ = 2400.0   # the clock the peaks above assume
 PEAK_HBM_GBS = 8000.0
 
 
@@ -131,6 +141,97 @@ def cpu_baseline_small(mats, real_shape=None):
             "sample": f"the whole batch ({len(mats)} matrices, 5 steps each)"}
 
 
+class GpuClockSampler:
+    """Graphics clock per XCD and socket power of the GPU that torch calls
+    cuda:0, from the AMD SMI library's gpu_metrics table, sampled every
+    `period` seconds by a host thread (reads only: no GPU work, no HIP calls).
+    The firmware refreshes the table every few hundred ms, so a sample is the
+    latest snapshot. `mark()` opens the window the summary covers."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period = period
+        self.samples = []
+        self.t_mark = None
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            import torch
+            self._smi = amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            props = torch.cuda.get_device_properties(0)
+            want = (int(getattr(props, "pci_domain_id", 0)), int(props.pci_bus_id), int(props.pci_device_id))
+            self._handle = None
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)   # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._handle = h
+            if self._handle is None:
+                raise RuntimeError(f"no SMI device at PCI {want}")
+            cap = amdsmi.amdsmi_get_power_cap_info(self._handle).get("power_cap")
+            self.power_cap_w = cap / 1e6 if isinstance(cap, (int, float)) else None
+        except Exception as e:  # the figure is optional: report why it is missing
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _run(self):
+        import time as _t
+        while not self._stop.is_set():
+            t = _t.perf_counter()
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+                clks = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float))]
+                pw = m.get("current_socket_power")
+                self.samples.append((t, clks, pw if isinstance(pw, (int, float)) else None))
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self.error is None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def mark(self):
+        self.t_mark = time.perf_counter()
+
+    def stop(self, t_end):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=5)
+        try:
+            self._smi.amdsmi_shut_down()
+        except Exception:
+            pass
+        win = [x for x in self.samples if self.t_mark is not None and self.t_mark <= x[0] <= t_end]
+        note = None
+        if not win and self.t_mark is not None:
+            # a pass shorter than the sampling period: the snapshot in effect
+            # when it began
+            before = [x for x in self.samples if x[0] < self.t_mark]
+            win = before[-1:]
+            note = "timed pass shorter than the sampling period: the last sample before it"
+        if self.error is not None or not win:
+            return {"error": self.error or "no sample before the end of the timed pass"}
+        import statistics
+        mean_clk = [statistics.fmean(c) for _, c, _ in win if c]
+        per_xcd = [statistics.median(v) for v in zip(*[c for _, c, _ in win if c])]
+        power = [p for _, _, p in win if p is not None]
+        return {
+            "source": "AMD SMI gpu_metrics (current_gfxclks, current_socket_power)",
+            "samples": len(win),
+            "gfxclk_mhz": round(statistics.median(mean_clk), 1) if mean_clk else None,
+            "gfxclk_mhz_per_xcd": [round(v) for v in per_xcd],
+            "socket_power_w": round(statistics.median(power), 1) if power else None,
+            "power_cap_w": self.power_cap_w,
+            **({"note": note} if note else {}),
+        }
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -151,6 +252,24 @@ def tile_flops_per_kind(shapes, dtype):
         tiles, edge = ns.plan_tiles(shapes, dtype, stage)
         f[kind] = int(sum(2 * edge * edge * int(t[3]) for t in tiles))
     return f
+
+
+def small_executed_flops(shapes, steps=5):
+    """fp64 FLOPs the small-matrix kernel executes per call: per matrix (m =
+    min dim rounded up to 8 rows, n columns) the norm's m n FMAs, the Gram
+    matrix's m^2 n, the final product's m^2 n, and in every 512-column slice
+    the steps' 32 x 32 products (4 steps - 3 of them, 32^3 FMAs each; every
+    slice runs them, for n <= 131072)."""
+    total = 0
+    nprod = 4 * steps - 3 if steps > 0 else 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        if m == 0:
+            continue
+        mr = -(-m // 8) * 8
+        slices = -(-n // 512)
+        total += 2 * (mr * n + 2 * mr * mr * n + slices * nprod * 32 ** 3)
+    return total
 
 
 def pass_bytes(shapes, elt):
@@ -298,6 +417,8 @@ def main():
                 dst.copy_(src)
         torch.cuda.synchronize()
 
+    sampler = GpuClockSampler()
+    sampler.start()
     for w in range(args.warmup):
         ns.orthogonalize(batches[w % nbatch])
         torch.cuda.synchronize()
@@ -307,11 +428,13 @@ def main():
     # timed pass: K calls, each on its own pristine copy, no profiling events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    sampler.mark()
     for k in range(args.steps):
         ns.orthogonalize(batches[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    gpu_clock = sampler.stop(t1)
     log(f"timed {args.steps} steps in {elapsed:.3f} s")
 
     # profiling pass: per-kernel HIP events on the call's stream
@@ -343,15 +466,18 @@ def main():
             entry["pct_hbm_peak"] = round(100 * bytes_kind[kind] / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
         kernels[kind] = entry
     if small_batch:
-        # the small-path kernel does the whole iteration in fp32 on the vector
-        # ALUs, in one launch per phase: metric FLOPs of the padded batch per
-        # call over the kernel time of a call, against the fp32 vector peak
+        # the small-path kernel evaluates the iteration in fp64, in one launch
+        # per phase: the metric FLOPs of the batch as passed per call over the
+        # kernel time of a call, against the fp64 peak; beside it the fp64
+        # FLOPs the kernel executes
         dom = "small"
         kernels[dom]["ms_per_call"] = round(kernels[dom]["ms_total"] / nprof, 4)
-        achieved = sum(wl.flops_per_matrix(r, c) for r, c in shapes) / (kernels[dom]["ms_per_call"] * 1e-3) / 1e12
+        call_s = kernels[dom]["ms_per_call"] * 1e-3
+        achieved = sum(wl.flops_per_matrix(r, c) for r, c in shapes) / call_s / 1e12
+        kernels[dom]["executed_fp64_tflops"] = round(small_executed_flops(shapes) / call_s / 1e12, 3)
         roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
-                    "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_FP32_VALU_TFLOPS, 5), "traffic": None}
+                    "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_FP64_TFLOPS, 5), "traffic": None}
     else:
         dom = max((k for k in kernels if k in per_kind), key=lambda k: kernels[k]["ms_total"])
         # the dominant kernel's algorithmic FLOPs per launch (for the update,
@@ -377,7 +503,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if small_batch or fp32 else "bf16",
+        "dtype": "f64" if small_batch else "f32" if fp32 else "bf16",
         "data": "synthetic",
         "config": desc,
         "tflops": round(tflops, 1),
@@ -399,6 +525,12 @@ def main():
             "tiles_tflops": round(tiles_all / step_s / 1e12, 1),
             "tiles_pct_peak": round(100 * tiles_all / step_s / 1e12 / peak_main, 2),
         }
+    if gpu_clock.get("gfxclk_mhz"):
+        # the roofline's peak scaled to the clock the chip sustained
+        scaled = roofline["peak"] * gpu_clock["gfxclk_mhz"] / PEAK_CLOCK_MHZ
+        gpu_clock["roofline_peak_at_this_clock"] = round(scaled, 1)
+        gpu_clock["roofline_frac_at_this_clock"] = round(roofline["achieved"] / scaled, 4)
+    out["gpu_clock"] = gpu_clock
     acc = accuracy_vs_stored_oracle(args.workload, ref_inputs, batches[args.steps - 1])
     if acc is not None:
         out["accuracy"] = acc
