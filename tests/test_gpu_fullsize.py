@@ -18,7 +18,7 @@ import torch
 
 import newton_schulz_04_amd as ns
 from newton_schulz_04_amd import workloads
-from nsutil import GOLDEN, check_against_golden, load_golden, zero_bits
+from nsutil import GOLDEN, TOL, check_against_golden, load_golden, zero_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,29 @@ def test_dense_lowrank_batch():
     # the same matrix alone gives the same bits
     alone = _run([mats[idx[0]]])[0]
     assert torch.equal(alone.view(torch.int16), out[idx[0]].view(torch.int16))
+
+
+def test_dense_lowrank_fp32_batch():
+    # The fp32 path on the same eight matrices, as the benchmark's fp32
+    # workload passes them: the bf16 values widened exactly to fp32, so the
+    # stored oracle samples of the bf16 inputs are this input's too. The
+    # specification's fp32 bar (relative Frobenius error <= 1e-4) on the
+    # sampled rows, columns, sketch and norm.
+    idx = _golden_indices("dense_lowrank")
+    if not idx:
+        pytest.skip("no stored oracle sample for dense_lowrank")
+    mats = [workloads.dense_lowrank_matrix(i) for i in range(workloads.DENSE_COUNT)]
+    out = _run([m.float() for m in mats])
+    for y in out:
+        assert y.dtype == torch.float32 and bool(torch.isfinite(y).all())
+    for i in idx:
+        g = load_golden(f"dense_lowrank_{i}")
+        assert str(g["input_sha256"]) == workloads.sha256(mats[i])
+        e = check_against_golden(out[i].cpu(), g, tol=TOL[torch.float32])
+        print(f"fp32 dense_lowrank_{i}: rows {e[0]:.3e} sketch {e[1]:.3e} norm {e[2]:.3e} "
+              f"worst row/col {e[3]:.3e}", flush=True)
+    alone = _run([mats[idx[0]].float()])[0]
+    assert torch.equal(alone.view(torch.int32), out[idx[0]].view(torch.int32))
 
 
 def test_ragged_remainder_batches():
