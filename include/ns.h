@@ -32,13 +32,19 @@
  *    result is rounded to bf16 (round-to-nearest-even). Relative Frobenius
  *    error against an fp64 evaluation of the same iteration: a few 1e-3 on
  *    the shapes tested, within 2e-2.
- *  - bf16 matrices with min(rows, cols) <= 32: the whole iteration in fp32
- *    on the vector units, result rounded to bf16.
- *  - fp32 matrices: fp32 arithmetic throughout (fp32 MFMA for the tiled
- *    path), within 1e-4 of the fp64 evaluation.
- *  - The norm sums squares in fp32 with per-piece power-of-two scaling, so
- *    every finite input normalizes (entries up to FLT_MAX); an Inf or NaN
- *    entry propagates (see ns_orthogonalize_batched).
+ *  - matrices of either dtype with min(rows, cols) <= 32 (the small-matrix
+ *    path, see NS_SMALL_M): the iteration evaluated in fp64 through the m x m
+ *    Gram matrix, which reaches the same result up to rounding: with
+ *    X_k = Q_k X_0, A_0 = X_0 X_0^T over the n columns, then per step
+ *    B'_k = a I + b A_k + c A_k^2, Q_(k+1) = B'_k Q_k and
+ *    A_(k+1) = B'_k A_k B'_k on m x m matrices, and finally Q X_0, rounded to
+ *    the buffer's dtype.
+ *  - fp32 matrices with min(rows, cols) > 32: fp32 arithmetic throughout
+ *    (fp32 MFMA), within 1e-4 of the fp64 evaluation.
+ *  - The tiled path's norm sums squares in fp32 with per-piece power-of-two
+ *    scaling, the small path's in fp64, so every finite input normalizes
+ *    (entries up to FLT_MAX); an Inf or NaN entry propagates (see
+ *    ns_orthogonalize_batched).
  * Zero rows and columns of G come back as exact +0.0, and a matrix gives the
  * same bits alone, in any batch, at any position and with trailing zero rows
  * appended.
@@ -124,8 +130,8 @@ typedef enum {
  *   NS_EINVAL  negative count, steps or dimension; NULL ptrs/shapes with
  *              count > 0; NULL pointer for a non-empty matrix; a pointer not
  *              aligned to the element size; NULL coeffs with steps > 0; a
- *              dimension above 2^24; a tiled-path matrix (min(rows, cols) >
- *              32) whose padded operand is too large for 32-bit buffer
+ *              dimension above 2^24; a tiled-path matrix (min(rows, cols)
+ *              above the small-path threshold) whose padded operand is too large for 32-bit buffer
  *              offsets: with m, n rounded up to multiples of 256 (mp, np),
  *              np x mp x element size must stay below 2 GiB and
  *              np x 256 x element size below 2 GiB (e.g. 32768 x 32768 bf16
@@ -305,8 +311,9 @@ int64_t ns_compute_cost(int64_t rows, int64_t cols);
 /*
  * Host-only view of the batch plan, for tests and tools.
  *
- * ns_plan_classify: kinds[i] = 0 (empty), 1 (small: whole iteration in one
- * workgroup, fp32), 2 (large: tiled MFMA path).
+ * ns_plan_classify: kinds[i] = 0 (empty), 1 (small: min(rows, cols) <= the
+ * NS_SMALL_M threshold, the fp64 Gram-form kernel, one workgroup per
+ * 512-column slice), 2 (large: tiled MFMA path).
  *
  * ns_plan_tiles: the tile list of one grouped GEMM stage in launch order.
  *   stage 0 = A = X X^T (upper-triangle tiles), 1 = B = bA + cA^2 (same

@@ -11,7 +11,7 @@ namespace ns {
 constexpr int kTile = 256;
 // Matrices with min(rows, cols) <= kSmallMax (or the NS_SMALL_M environment
 // variable's lower threshold, see small_threshold) run the small-matrix
-// kernel in fp32.
+// kernel, which works in fp64.
 constexpr int kSmallMax = 32;
 // Elements per workgroup in the norm's partial-sum pass.
 constexpr int kNormChunk = 16384;

@@ -10,7 +10,8 @@
 //                  on m x m matrices, one product at the end); one 512-thread
 //                  workgroup per 512-column slice, three launches.
 //   k_norm_partial sum of squares of a 16K-element piece of G (wave shuffles).
-//   k_norm_final   folds the pieces of a matrix in fixed order -> 1/(||G||+eps).
+//   k_norm_final   folds the pieces of a matrix in fixed order -> 1/(||G||+eps)
+//                  (with a power-of-two prescale for entries of 2^40 or more).
 //   k_prep         X = G/(||G||+eps), transposed when rows > cols, zero-padded
 //                  to multiples of 256; writes X^T (bf16: X_hi = bf16(X) in
 //                  column panels of 32 and X_lo = bf16(X - X_hi) row-major;
@@ -203,8 +204,9 @@ __device__ __forceinline__ float block_max(float v, float* red4)
 // them polynomials in A0, so symmetric and commuting), A_{k+1} =
 // B'_k A_k B'_k. The small path evaluates the iteration in that form: one
 // Gram matrix A0 = X0 X0^T over the n columns, the steps on m x m matrices,
-// and one product Q X0 at the end: 3 m^2 n + O(m^3) operations instead of
-// 4 m^2 n per step, and three launches whatever the step count. In exact
+// and one product Q X0 at the end: 2 m^2 n + O(m^3) multiply-adds in all
+// instead of 2 m^2 n + m^3 per step, and three launches whatever the step
+// count. In exact
 // arithmetic it is the iteration itself; it runs in fp64 (whose vector rate
 // equals the unpacked fp32 one), so only the final rounding to the
 // caller's dtype is visible.

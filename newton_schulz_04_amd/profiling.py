@@ -43,14 +43,25 @@ SIMDS_PER_CU = 4
 TRAFFIC_SOURCES = ("ns_kernels.hip", "ns_internal.h", "ns_plan.cpp", "ns_plan.h")
 
 
+def code_only(text):
+    """C/C++ source without its comments and with whitespace runs collapsed:
+    what the compiler sees, so that an edit to a comment does not count as a
+    change of the kernels. (The hashed sources hold no comment markers inside
+    string literals.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash():
-    """sha256 over the kernel and planner sources (TRAFFIC_SOURCES)."""
+    """sha256 over the code (comments excluded) of the kernel and planner
+    sources (TRAFFIC_SOURCES)."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
         if os.path.basename(path) in TRAFFIC_SOURCES:
             h.update(os.path.basename(path).encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(code_only(f.read()).encode())
     return h.hexdigest()
 
 
@@ -106,7 +117,9 @@ def traffic(fetch_csv, write_csv, command):
                          "fetch_bytes": round(fb) if fb is not None else None,
                          "write_bytes": round(wb) if wb is not None else None,
                          "bytes": round(fb + wb) if fb is not None and wb is not None else None}
-    return {"source_sha256": source_hash(), "command": command,
+    return {"source_sha256": source_hash(),
+            "source_hash_of": "the code of " + ", ".join(TRAFFIC_SOURCES) + " without comments (code_only)",
+            "command": command,
             "copy_probe": {"bytes": COPY_PROBE_BYTES, "fetch_kib": probe_f, "write_kib": probe_w,
                            "fetch_scale": round(sf, 4), "write_scale": round(sw, 4)},
             "kernels": kernels}

@@ -82,3 +82,16 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stdout and "--gpus" in r.stderr
+
+
+def test_traffic_record_is_keyed_to_the_code_not_its_comments():
+    from newton_schulz_04_amd.profiling import code_only
+    a = "int f(int x) { // doubles x\n    return 2 * x; /* the\n result */ }\n"
+    b = "int f(int x) {   // twice x, reworded\n  return 2 * x;  }"
+    c = "int f(int x) { return 3 * x; }"
+    assert code_only(a) == code_only(b) == "int f(int x) { return 2 * x; }"
+    assert code_only(c) != code_only(a)
+    # the committed dense-batch record matches the current sources, so the
+    # bench reports its traffic
+    assert bench.measured_traffic("dense_lowrank", "update") is not None
+    assert bench.measured_traffic("no_such_workload", "update") is None

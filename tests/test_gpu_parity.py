@@ -246,7 +246,7 @@ def test_contract_errors_leave_buffers_untouched():
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shape", [(32, 2304), (33, 2304), (2304, 32), (2304, 33)])
 def test_small_large_boundary(dtype, shape):
-    # m = 32 is the last fused small-path size, m = 33 the first tiled one
+    # m = 32 is the last small-path size, m = 33 the first tiled one
     g = workloads.gaussian(shape, seed=41, index=shape[0], dtype=dtype)
     (y,) = gpu_run([g])
     assert rel_err(y, oracle_run(g)) <= TOL[dtype]
@@ -255,13 +255,13 @@ def test_small_large_boundary(dtype, shape):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shape", [(24, 1024), (24, 1025), (1025, 24), (32, 796), (32, 797), (5, 2389),
                                    (5, 4000)])
-def test_small_path_resident_and_streamed(dtype, shape):
-    # The fused small-matrix kernel keeps X in LDS while n x (m rounded up to
-    # 8, plus 4) floats fit 28672 (24 x 1024, 32 x 796 and 5 x 2389 are the
-    # largest such), else streams it from an L2-resident buffer in 128-column
-    # chunks (24 x 1025, 32 x 797, 5 x 4000; ragged last chunks). Both paths,
-    # alone and in one batch, against the oracle; a matrix's path and bits do
-    # not depend on the batch.
+def test_small_path_slices(dtype, shape):
+    # The small-matrix kernel gives each 512-column slice of X its own
+    # workgroup (its Gram piece in 256-column chunks) and sums the pieces in
+    # slice order: two whole slices (24 x 1024), a last slice of one column
+    # (24 x 1025 and its transpose), ragged last slices and chunks (32 x 796,
+    # 32 x 797, 5 x 2389), eight slices (5 x 4000). Alone and in one batch,
+    # against the oracle; a matrix's bits do not depend on the batch.
     g = workloads.gaussian(shape, seed=43, index=shape[0] * 7 + shape[1], dtype=dtype)
     (y,) = gpu_run([g])
     assert rel_err(y, oracle_run(g)) <= TOL[dtype]
