@@ -12,6 +12,7 @@ import torch
 
 import newton_schulz_04_amd as ns
 from newton_schulz_04_amd import workloads
+from nsutil import TOL, oracle_run, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +105,58 @@ def test_host_threads_on_their_own_streams():
         assert got is not None
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_release_workspace_while_work_is_in_flight():
+    # ns_release_workspace frees the device workspace with stream-ordered
+    # frees: released right after a call is enqueued (the stream still busy),
+    # the call completes with its own bits, and the next call on the stream
+    # allocates a fresh workspace in stream order
+    stream = torch.cuda.Stream()
+    first = [workloads.gaussian((2048, 2304), seed=74, index=i) for i in range(4)]
+    second = [workloads.gaussian((1024, 1536), seed=75, index=i) for i in range(3)] + \
+             [workloads.gaussian((24, 700), seed=75, index=9)]
+    want = []
+    for batch in (first, second):
+        dev = [g.cuda() for g in batch]
+        ns.orthogonalize(dev)
+        torch.cuda.synchronize()
+        want.append([d.cpu() for d in dev])
+    with torch.cuda.stream(stream):
+        a = [g.cuda() for g in first]
+        b = [g.cuda() for g in second]
+        torch.cuda.synchronize()
+        ns.orthogonalize(a, stream=stream)
+        in_flight = not stream.query()
+        ns.release_workspace(stream)
+        ns.orthogonalize(b, stream=stream)
+        ns.release_workspace(stream)
+    stream.synchronize()
+    assert in_flight, "the first call finished before the release: nothing was in flight"
+    for got, exp in zip((a, b), want):
+        for x, y in zip(got, exp):
+            assert torch.equal(x.cpu().view(torch.int16), y.view(torch.int16))
+
+
+def test_more_batches_than_the_plan_cache_holds():
+    # 72 distinct batches in a row (the cache keeps 64 plans per stream), then
+    # some of them again: evicted plans are rebuilt and give the same bits
+    batches = [[workloads.gaussian((40 + i % 5, 300), seed=76, index=2 * i),
+                workloads.gaussian((20, 260 + i), seed=76, index=2 * i + 1)] for i in range(72)]
+    devs = [[g.cuda() for g in b] for b in batches]
+    for d in devs:
+        ns.orthogonalize(d)
+    torch.cuda.synchronize()
+    first = [[x.cpu() for x in d] for d in devs]
+    again = (0, 1, 71)
+    for i in again:
+        for x, g in zip(devs[i], batches[i]):
+            x.copy_(g)
+        ns.orthogonalize(devs[i])
+    torch.cuda.synchronize()
+    for i in again:
+        for x, y in zip(devs[i], first[i]):
+            assert torch.equal(x.cpu().view(torch.int16), y.view(torch.int16)), i
+    for i in (0, 35):
+        for x, g in zip(first[i], batches[i]):
+            assert rel_err(x, oracle_run(g)) <= TOL[torch.bfloat16]
