@@ -5,7 +5,9 @@
 // context holds a large enough workspace, finds or uploads the batch's
 // metadata block, and enqueues the kernel sequence on the caller's stream:
 //
-//   small matrices : k_small (one launch for all of them)
+//   small matrices : k_small per group of matrices with one row count MR:
+//                    norm pieces, Gram pieces, the steps and the result (three
+//                    launches; one when every matrix of the group is one slice)
 //   large matrices : norm pieces, norm fold, normalize/transpose/pad, then per
 //                    step the three grouped GEMM stages X X^T, bA + cA^2,
 //                    aX + BX (the last one writes the caller's buffers); a
