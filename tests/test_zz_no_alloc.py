@@ -2,7 +2,7 @@
 against ns_orthogonalize_batched through the C ABI: the same bits, on two
 calls in a row, the second with a smaller batch, for both dtypes; a batch
 that does not fit the static scratch array is rejected before anything is
-enqueued."""
+enqueued; the call captured into a HIP graph replays with the eager bits."""
 import pytest
 import torch
 
@@ -65,3 +65,31 @@ def test_noalloc_rejects_a_batch_larger_than_the_scratch():
     # and a batch that fits still runs after the rejection
     a, b = _both([workloads.gaussian((300, 520), seed=85)])
     assert torch.equal(_bits(a[0]), _bits(b[0]))
+
+
+def test_noalloc_under_hip_graph_capture():
+    # What the entry point is for: captured into a HIP graph (its launches
+    # are kernels only: no allocation, no memset, no copy), then replayed on
+    # fresh inputs, with eager work that uses the same scratch array and
+    # synchronizations between the replays; every replay gives the eager
+    # call's bits
+    shapes = [(24, 2304), (300, 520), (520, 300)]
+    pristine = [workloads.gaussian(s, seed=86, index=i).cuda() for i, s in enumerate(shapes)]
+    eager = [p.clone() for p in pristine]
+    ns.orthogonalize(eager, noalloc=True)   # (also looks the scratch address up, before any capture)
+    torch.cuda.synchronize()
+    bufs = [p.clone() for p in pristine]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ns.orthogonalize(bufs, noalloc=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for b, p in zip(bufs, pristine):
+            b.copy_(p)
+        other = [workloads.gaussian((40, 300), seed=87, index=rep).cuda()]
+        ns.orthogonalize(other, noalloc=True)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert torch.equal(_bits(b), _bits(e)), rep
