@@ -12,7 +12,7 @@
 //                    step the three grouped GEMM stages X X^T, bA + cA^2,
 //                    aX + BX (the last one writes the caller's buffers); a
 //                    bf16 symmetric stage whose last round is split runs its
-//                    half tiles as a second launch.
+//                    half tiles after the whole ones in the same launch.
 //
 // Nothing here waits for the device. Workspace growth uses stream-ordered
 // allocation (hipMallocAsync / hipFreeAsync); metadata goes up from pinned
@@ -584,14 +584,10 @@ ns_status enqueue_launches(const Plan& p, char* meta, int32_t steps, const float
         return hip_fail(e, "normalize kernel launch");
     const int nu = (int)p.update_tiles.size();
     // a symmetric stage: its whole tiles, then (when its last round is
-    // split) the half tiles, one timed launch pair
+    // split) the half tiles, in one launch
     auto sym = [&](int stage, const ns::Tile* tl, int n, int split, int cur, int last, float ca, float cb,
                    float cc) {
-        hipError_t r = ns::launch_gemm(dtype, stage, large, tl, n - split, cur, last, 0, ca, cb, cc, stream);
-        if (r == hipSuccess && split > 0)
-            r = ns::launch_gemm(dtype, stage, large, tl + (n - split), 2 * split, cur, last, 1, ca, cb, cc,
-                                stream);
-        return r;
+        return ns::launch_gemm(dtype, stage, large, tl, n + split, n - split, cur, last, ca, cb, cc, stream);
     };
     for (int s = 0; s < steps; ++s) {
         const int cur = s & 1, last = s == steps - 1;
@@ -605,7 +601,7 @@ ns_status enqueue_launches(const Plan& p, char* meta, int32_t steps, const float
             });
         if (e == hipSuccess)
             e = timed(ns::kKindUpdate, stream, [&] {
-                return ns::launch_gemm(dtype, 2, large, upd, nu, cur, last, 0, ca, cb, cc, stream);
+                return ns::launch_gemm(dtype, 2, large, upd, nu, nu, cur, last, ca, cb, cc, stream);
             });
         if (e != hipSuccess)
             return hip_fail(e, "GEMM kernel launch");

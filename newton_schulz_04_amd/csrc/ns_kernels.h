@@ -53,10 +53,12 @@ hipError_t launch_scale_out(int dtype, const LargeMat* mats, int nmats,
 //   stage 1: B = b A + c A A    (upper-triangle tiles, mirrored)
 //   stage 2: X <- a X + B X     (all tiles); `last` writes the caller buffer
 // `cur` selects the X operand slot read (the other slot is written).
-// half (bf16 stages 0 and 1): the tiles are half tiles (bit 30 of the matrix
-// index selects which half of an off-diagonal tile's columns).
+// tiles[0, nwhole) are whole tiles; tiles[nwhole, ntiles) (bf16 stages 0 and
+// 1 only, else nwhole == ntiles) are half tiles (bit 30 of the matrix index
+// selects which half of an off-diagonal tile's columns), run in the same
+// launch after the whole ones.
 hipError_t launch_gemm(int dtype, int stage, const LargeMat* mats,
-                       const Tile* tiles, int ntiles, int cur, int last, int half,
+                       const Tile* tiles, int ntiles, int nwhole, int cur, int last,
                        float a, float b, float c, hipStream_t stream);
 
 }  // namespace ns

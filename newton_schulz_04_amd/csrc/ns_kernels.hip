@@ -17,13 +17,14 @@
 //                  column panels of 32 and X_lo = bf16(X - X_hi) row-major;
 //                  fp32: X^T and X), through a 64x64 LDS tile where it must
 //                  transpose.
-//   k_gemm<dtype, stage, last, half>
+//   k_gemm<dtype, stage, last, split>
 //                  grouped 256x256 MFMA GEMM over a tile list, C = P Q^T:
 //                    stage 0  P = Q = X            -> A (upper tiles, mirrored)
 //                    stage 1  P = Q = A (= A^T)    -> B = bA + cA^2 (mirrored)
 //                    stage 2  P = B, Q = X^T store -> X = aX + BX
-//                  last: the final update writes the caller's buffer; half:
-//                  the half tiles of a symmetric stage's split last round.
+//                  last: the final update writes the caller's buffer; split:
+//                  a symmetric stage whose last round runs as half tiles,
+//                  after the whole tiles in the same grid.
 //   k_scale_out    steps == 0: G <- G/(||G||+eps).
 //
 // Every sum has a fixed order that does not depend on the batch, on the
@@ -1338,6 +1339,8 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
     tile_store(ws, out + gbi * ld + gbj, ld, wave, lane, kHalf ? hsel : -1);
 }
 
+// One workgroup's tile t of a grouped GEMM stage, with the workgroup's LDS
+// slots (sl0 .. sl3 the ring, lo3 the epilogue block's quarter 3).
 // HALF (bf16 X X^T and bA + cA^2 only): the workgroup computes half of an
 // off-diagonal tile's columns, those in 64-column pieces 2 hsel and 2 hsel + 2
 // (wavefront column wc takes its 32-column blocks 2 hsel and 2 hsel + 1);
@@ -1345,26 +1348,12 @@ __device__ __forceinline__ void sym_epilogue_bf16(const LargeMat& M, char* s0, c
 // sequence as in a whole tile, so the bits are the same; the half tiles of a
 // launch's last, partial round run on twice as many compute units.
 template <int DT, int STAGE, int LAST, int HALF>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
-                                                      const Tile* __restrict__ tiles, int cur,
-                                                      int last, float ca, float cb, float cc)
+__device__ __forceinline__ void gemm_tile(const LargeMat* __restrict__ mats, const Tile t, int cur, int last,
+                                          float ca, float cb, float cc, char* sl0, char* sl1, char* sl2,
+                                          char* sl3, char* lo3)
 {
     using OpT = typename Elt<DT>::type;
     constexpr int NJ = HALF ? 2 : 4;   // 32-column blocks per wavefront
-    // Four LDS slots (P then Q, 16 KB each), one object each: with the k loop
-    // unrolled over the ring, every LDS read and every DMA names its slot
-    // statically, so the compiler can see that a refill does not touch the
-    // slots being read and does not wait for them.
-    __shared__ __attribute__((aligned(1024))) char sl0[2 * kSlotOpBytes];
-    __shared__ __attribute__((aligned(1024))) char sl1[2 * kSlotOpBytes];
-    __shared__ __attribute__((aligned(1024))) char sl2[2 * kSlotOpBytes];
-    __shared__ __attribute__((aligned(1024))) char sl3[2 * kSlotOpBytes];
-    // bf16 update and bA + cA^2 only: quarter 3 of the epilogue's block,
-    // loaded before the K loop so that the epilogue need not wait for it
-    // (160 KB of LDS in all)
-    __shared__ __attribute__((aligned(1024))) char lo3[2 * kSlotOpBytes];
-
-    const Tile t = tiles[blockIdx.x];
     const int hsel = HALF ? (int)((uint32_t)t.mat >> 30) : 0;
     const int jbase = 2 * hsel;
     const LargeMat& M = mats[HALF ? (t.mat & 0x3FFFFFFF) : t.mat];
@@ -1892,32 +1881,64 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     }
 }
 
+// A grouped GEMM stage over tiles[0 .. ntiles): one workgroup per tile.
+// SPLIT (bf16 X X^T and bA + cA^2): workgroups [0, nwhole) run whole tiles
+// and the rest the half tiles of the stage's split last round; being in the
+// same grid, the half tiles go to the compute units that finish their whole
+// tiles first.
+template <int DT, int STAGE, int LAST, int SPLIT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict__ mats,
+                                                      const Tile* __restrict__ tiles, int cur, int last,
+                                                      float ca, float cb, float cc, int nwhole)
+{
+    // Four LDS slots (P then Q, 16 KB each), one object each: with the k loop
+    // unrolled over the ring, every LDS read and every DMA names its slot
+    // statically, so the compiler can see that a refill does not touch the
+    // slots being read and does not wait for them.
+    __shared__ __attribute__((aligned(1024))) char sl0[2 * kSlotOpBytes];
+    __shared__ __attribute__((aligned(1024))) char sl1[2 * kSlotOpBytes];
+    __shared__ __attribute__((aligned(1024))) char sl2[2 * kSlotOpBytes];
+    __shared__ __attribute__((aligned(1024))) char sl3[2 * kSlotOpBytes];
+    // bf16 update and bA + cA^2 only: quarter 3 of the epilogue's block,
+    // loaded before the K loop so that the epilogue need not wait for it
+    // (160 KB of LDS in all)
+    __shared__ __attribute__((aligned(1024))) char lo3[2 * kSlotOpBytes];
+
+    const Tile t = tiles[blockIdx.x];
+    if (SPLIT && (int)blockIdx.x >= nwhole)
+        gemm_tile<DT, STAGE, LAST, 1>(mats, t, cur, last, ca, cb, cc, sl0, sl1, sl2, sl3, lo3);
+    else
+        gemm_tile<DT, STAGE, LAST, 0>(mats, t, cur, last, ca, cb, cc, sl0, sl1, sl2, sl3, lo3);
+}
+
 template <typename OpT, int STAGE>
-hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, int cur, int last, int half,
+hipError_t launch_gemm_t(const LargeMat* mats, const Tile* tiles, int ntiles, int nwhole, int cur, int last,
                          float a, float b, float c, hipStream_t stream)
 {
     // The bf16 update's last step (it writes the caller's buffer) is its own
     // instantiation, so the other steps' epilogue carries no code for it; so
-    // are the half tiles of the bf16 symmetric stages.
+    // is a bf16 symmetric stage with half tiles.
     constexpr int DT = IsBf16<OpT>::value ? 0 : 1;
+    if (nwhole < 0 || nwhole > ntiles)
+        return hipErrorInvalidValue;
     if constexpr (STAGE == 2 && DT == 0) {
         if (last) {
             hipLaunchKernelGGL((k_gemm<DT, STAGE, 1, 0>), dim3(ntiles), dim3(kThreads), 0, stream, mats,
-                               tiles, cur, last, a, b, c);
+                               tiles, cur, last, a, b, c, ntiles);
             return hipGetLastError();
         }
     }
     if constexpr (STAGE < 2 && DT == 0) {
-        if (half) {
+        if (nwhole < ntiles) {
             hipLaunchKernelGGL((k_gemm<DT, STAGE, 0, 1>), dim3(ntiles), dim3(kThreads), 0, stream, mats,
-                               tiles, cur, last, a, b, c);
+                               tiles, cur, last, a, b, c, nwhole);
             return hipGetLastError();
         }
     }
-    if (half)
+    if (nwhole < ntiles)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_gemm<DT, STAGE, 0, 0>), dim3(ntiles), dim3(kThreads), 0, stream, mats, tiles,
-                       cur, last, a, b, c);
+                       cur, last, a, b, c, ntiles);
     return hipGetLastError();
 }
 }  // namespace
@@ -1995,17 +2016,17 @@ hipError_t launch_scale_out(int dtype, const LargeMat* mats, int nmats, const in
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype, int stage, const LargeMat* mats, const Tile* tiles, int ntiles,
-                       int cur, int last, int half, float a, float b, float c, hipStream_t stream)
+hipError_t launch_gemm(int dtype, int stage, const LargeMat* mats, const Tile* tiles, int ntiles, int nwhole,
+                       int cur, int last, float a, float b, float c, hipStream_t stream)
 {
     if (dtype == 0) {
-        if (stage == 0) return launch_gemm_t<bf16, 0>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
-        if (stage == 1) return launch_gemm_t<bf16, 1>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
-        return launch_gemm_t<bf16, 2>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
+        if (stage == 0) return launch_gemm_t<bf16, 0>(mats, tiles, ntiles, nwhole, cur, last, a, b, c, stream);
+        if (stage == 1) return launch_gemm_t<bf16, 1>(mats, tiles, ntiles, nwhole, cur, last, a, b, c, stream);
+        return launch_gemm_t<bf16, 2>(mats, tiles, ntiles, nwhole, cur, last, a, b, c, stream);
     }
-    if (stage == 0) return launch_gemm_t<float, 0>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
-    if (stage == 1) return launch_gemm_t<float, 1>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
-    return launch_gemm_t<float, 2>(mats, tiles, ntiles, cur, last, half, a, b, c, stream);
+    if (stage == 0) return launch_gemm_t<float, 0>(mats, tiles, ntiles, nwhole, cur, last, a, b, c, stream);
+    if (stage == 1) return launch_gemm_t<float, 1>(mats, tiles, ntiles, nwhole, cur, last, a, b, c, stream);
+    return launch_gemm_t<float, 2>(mats, tiles, ntiles, nwhole, cur, last, a, b, c, stream);
 }
 
 }  // namespace ns

@@ -138,11 +138,12 @@ int32_t split_tail(std::vector<Tile>& tl)
     return (int32_t)r;
 }
 
-// The uploaded list: tiles [0, n - r), then the halves of the last r. Tiles
-// k and k' of a group of 8 sat on XCD k mod 8; their halves go to positions
-// 16 g + k mod 8 and 16 g + c + k mod 8 of the half launch (c = the group's
-// size), i.e. the same XCD for whole groups, so two halves share their
-// operand blocks in one L2.
+// The uploaded list: tiles [0, n - r), then the halves of the last r, all
+// in one launch. Tiles k and k' of a group of 8 sat on XCD k mod 8; their
+// halves go to positions 16 g + k mod 8 and 16 g + c + k mod 8 of the half
+// part, which starts at n - r, a multiple of kCus and so of 8 (c = the
+// group's size), i.e. the same XCD for whole groups, so two halves share
+// their operand blocks in one L2.
 std::vector<Tile> run_list(const std::vector<Tile>& tl, int32_t split)
 {
     const size_t n = tl.size(), r = (size_t)split, t0 = n - r;

@@ -55,9 +55,9 @@ struct Plan {
     std::vector<Tile> poly_tiles;        // stage bA+cA^2 (upper tiles, K = mp)
     std::vector<Tile> update_tiles;      // stage aX+BX  (all tiles,   K = mp)
     // bf16: the last syrk_split / poly_split tiles of those lists (a launch's
-    // partial last round, off-diagonal) run as two half tiles each, in a
-    // second launch; *_run is the uploaded list: the other tiles, then the
-    // half tiles (bit 30 of the matrix index = which half).
+    // partial last round, off-diagonal) run as two half tiles each, after the
+    // other tiles in the same launch; *_run is the uploaded list: the other
+    // tiles, then the half tiles (bit 30 of the matrix index = which half).
     int32_t syrk_split = 0, poly_split = 0;
     std::vector<Tile> syrk_run, poly_run;
     std::vector<int32_t> part_prefix;    // size nlarge+1

@@ -67,13 +67,12 @@ def source_hash():
 
 def kernel_kind(name):
     """Short name of a kernel from its (demangled or mangled) name."""
-    # k_gemm<dtype, stage, last, half>: half tiles of a split last round
-    # are their own kind (<stage>_half)
+    # k_gemm<dtype, stage, last, split>: a split launch (whole tiles, then
+    # the half tiles of the last round) is the whole stage, the same kind
     m = (re.search(r"k_gemm<\s*\d+\s*,\s*(\d+)\s*(?:,\s*\d+\s*)?(?:,\s*(\d+)\s*)?>", name) or
          re.search(r"k_gemmI(?:Li\d+E|DF16b|f)Li(\d+)E(?:Li\d+E)?(?:Li(\d+)E)?", name))
     if m:
-        kind = GEMM_KINDS.get(m.group(1), "gemm" + m.group(1))
-        return kind + "_half" if m.group(2) == "1" else kind
+        return GEMM_KINDS.get(m.group(1), "gemm" + m.group(1))
     for short in ("k_norm_partial", "k_norm_final", "k_prep", "k_small", "k_scale_out"):
         if short in name:
             return short[2:]
@@ -210,12 +209,6 @@ def summary_md(stats_csv, traffic_json, bench_json, title, shapes, kt_command, m
         e = t["kernels"].get(k)
         if not e:
             continue
-        # a split last round's half tiles are a second launch of the stage
-        # (one per step, like the main launch): their bytes count with it
-        h = t["kernels"].get(k + "_half")
-        if h:
-            e = {"fetch_bytes": e["fetch_bytes"] + h["fetch_bytes"],
-                 "write_bytes": e["write_bytes"] + h["write_bytes"]}
         rate = ""
         if ks.get(k):
             rate = f"{(e['fetch_bytes'] + e['write_bytes']) / (ks[k] * 1e-3) / 1e12:.2f} TB/s"
@@ -237,14 +230,19 @@ twice the MFMA work they do; bench.py reports `tflops_tiles` (what the MFMAs
 execute) beside it.
 """
     cp = t["copy_probe"]
+    gc = b.get("gpu_clock") or {}
+    clock = ""
+    if gc.get("gfxclk_mhz"):
+        clock = (f" Under the profiler the AMD SMI library read the XCD clocks at "
+                 f"{gc['gfxclk_mhz']:.0f} MHz (per XCD {gc.get('gfxclk_mhz_per_xcd')}) and the socket at "
+                 f"{gc.get('socket_power_w')} W against a {gc.get('power_cap_w')} W cap over the timed pass.")
     return f"""# {title}
 
 One bench step = one `ns_orthogonalize_batched` call over the batch: norm_partial,
-norm_final, prep, then 5 x (syrk = `k_gemm<0, 0, 0, 0>` X X^T, poly = `k_gemm<0, 1, 0, 0>`
+norm_final, prep, then 5 x (syrk = `k_gemm<0, 0, 0, s>` X X^T, poly = `k_gemm<0, 1, 0, s>`
 bA + cA^2, update = `k_gemm<0, 2, 0, 0>` aX + BX; the fifth update is `k_gemm<0, 2, 1, 0>`,
-which writes the caller's buffer; syrk_half and poly_half = `k_gemm<0, 0|1, 0, 1>`
-run the half tiles of a split last round, a second launch of the stage, and
-count with it in the traffic table). `copy_probe` rows are the runtime's
+which writes the caller's buffer; s = 1 when the stage's last round is split,
+its half tiles running after the whole tiles in the same launch). `copy_probe` rows are the runtime's
 device copies (bench restores its inputs from a pristine copy before the timed
 pass and before the profiling pass, outside both).
 Run from the repository root with `export TMPDIR=/tmp` and the library built
@@ -257,7 +255,7 @@ The same run's bench line: value {b['value']} matrices/s (timed pass, no events)
 {b['tflops']} TFLOP/s ({b['pct_bf16_peak']}% of 2.5 PFLOP/s, the metric's 4m^2n + 2m^3
 convention; executed by the kernels: {b.get('executed', {}).get('tiles_tflops')} TFLOP/s); per-launch ms from
 HIP events on the launch stream in bench.py's separate profiling pass:
-{", ".join(f"{k} {v}" for k, v in ks.items())}.
+{", ".join(f"{k} {v}" for k, v in ks.items())}.{clock}
 
 ## HBM-side traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
 
@@ -271,9 +269,9 @@ caller's buffer instead of X_hi and X_lo):
 
 {chr(10).join(rows)}
 
-The record with a hash of the library sources is `{os.path.basename(traffic_json)}`;
-bench.py reports the dominant kernel's bytes as `roofline.traffic` only while
-the hash matches. prep and norm_partial are the HBM-bound passes (peak 8 TB/s).
+The record, keyed by a hash of the code of the kernel and planner sources
+(comments excluded), is `{os.path.basename(traffic_json)}`; bench.py reports
+the dominant kernel's bytes as `roofline.traffic` only while the hash matches. prep and norm_partial are the HBM-bound passes (peak 8 TB/s).
 {mfma}"""
 
 

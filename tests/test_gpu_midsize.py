@@ -3,8 +3,9 @@ take, against the live fp64 oracle, element by element.
 
 Paths that only batches of more than 256 tiles or 2048-multiple shapes reach:
   * the half tiles of a symmetric stage's split last round
-    (k_gemm<0, 0|1, 0, 1>): a launch of n > 256 tiles whose last round holds
-    r = n mod 256 <= 128 tiles runs those as 2r half tiles;
+    (k_gemm<0, 0|1, 0, 1>): a stage of n > 256 tiles whose last round holds
+    r = n mod 256 <= 128 tiles runs those as 2r half tiles after the whole
+    ones, in the same launch;
   * tile lists of more than one round (n > 256) in every stage;
   * padded row pitches: an operand row of 4096 bytes times an odd number
     gets 128 bytes of padding (bf16 m = 2048, 6144, 10240; fp32 rows of
