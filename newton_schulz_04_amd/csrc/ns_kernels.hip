@@ -1905,10 +1905,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const LargeMat* __restrict
     __shared__ __attribute__((aligned(1024))) char lo3[2 * kSlotOpBytes];
 
     const Tile t = tiles[blockIdx.x];
-    if (SPLIT && (int)blockIdx.x >= nwhole)
-        gemm_tile<DT, STAGE, LAST, 1>(mats, t, cur, last, ca, cb, cc, sl0, sl1, sl2, sl3, lo3);
-    else
-        gemm_tile<DT, STAGE, LAST, 0>(mats, t, cur, last, ca, cb, cc, sl0, sl1, sl2, sl3, lo3);
+    if constexpr (SPLIT) {
+        if ((int)blockIdx.x >= nwhole) {
+            gemm_tile<DT, STAGE, LAST, 1>(mats, t, cur, last, ca, cb, cc, sl0, sl1, sl2, sl3, lo3);
+            return;
+        }
+    }
+    gemm_tile<DT, STAGE, LAST, 0>(mats, t, cur, last, ca, cb, cc, sl0, sl1, sl2, sl3, lo3);
 }
 
 template <typename OpT, int STAGE>
