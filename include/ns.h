@@ -30,8 +30,9 @@
  *    with the rounding residues of their diagonals kept in fp32 and added
  *    back (first-order terms in B, the diagonal of B in the update). The
  *    result is rounded to bf16 (round-to-nearest-even). Relative Frobenius
- *    error against an fp64 evaluation of the same iteration: a few 1e-3 on
- *    the shapes tested, within 2e-2.
+ *    error against an fp64 evaluation of the same iteration: 2.6e-3 on the
+ *    dense low-rank 8192 x 6144 batch, 6e-3 to 1e-2 on Gaussian inputs, up
+ *    to 1.4e-2 on small nearly square ones; within 2e-2 at 5 steps.
  *  - matrices of either dtype with min(rows, cols) <= 32 (the small-matrix
  *    path, see NS_SMALL_M): the iteration evaluated in fp64 through the m x m
  *    Gram matrix, which reaches the same result up to rounding: with
